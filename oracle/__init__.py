@@ -1,0 +1,109 @@
+"""fp64 CPU oracle for the attention forward pass — TEST INFRASTRUCTURE.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never links or calls
+it, and it imports nothing from the GPU library.
+
+``attn_ref`` evaluates the plain, non-online reference ``softmax(Q K^T *
+scale) V`` per (batch, head) slice, plus the natural-log LSE, in double
+precision (VeriTile, "FlashAttention1.NaiveRefinement", section "Naive FA
+reference"; reduction order from tiny.accy.kernel.library.attention,
+``expectedOutput``).  The arithmetic lives in ``attn_ref.c``; this module only
+builds it with gcc and marshals numpy arrays through ctypes.
+
+Every function here is pinned by ``tests/test_oracle.py`` (library routine,
+high-precision brute force, closed forms, invariants, and planted mistakes).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "attn_ref.c")
+LIBRARY = os.path.join(_HERE, "liboracle_attn.so")
+
+_lib = None
+
+
+def build(force: bool = True, source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc (no fast-math: IEEE double semantics)."""
+    if force or not os.path.exists(output):
+        tmp = output + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+               "-fno-fast-math", "-ffp-contract=off", source, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, output)
+    return output
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    lib = ctypes.CDLL(path)
+    f = lib.attn_ref_f64
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64 = ctypes.c_int64
+    f.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64,
+                  ctypes.c_double, ctypes.c_int, ctypes.POINTER(i64), i64,
+                  ctypes.c_int]
+    f.restype = ctypes.c_int
+    return lib
+
+
+def _library() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = load_library(LIBRARY)
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def attn_ref(q, k, v, scale: float, causal: bool, rows=None, nthreads=None,
+             want_probs: bool = False, lib: ctypes.CDLL | None = None):
+    """Return ``(O, LSE)`` (and the softmax weights ``P`` if asked).
+
+    q: [B,H,S_q,D_qk], k: [B,H,S_k,D_qk], v: [B,H,S_k,D_v]; any float dtype,
+    converted exactly to float64.  ``rows`` restricts the computation to the
+    listed query rows (O then has shape [B,H,len(rows),D_v]).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B,H,S,D]")
+    B, H, S_q, D_qk = q.shape
+    if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != D_qk \
+            or v.shape[2] != k.shape[2]:
+        raise ValueError("inconsistent q/k/v shapes")
+    S_k, D_v = k.shape[2], v.shape[3]
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows.shape[0]
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    else:
+        n_rows, rows_p = S_q, None
+    o = np.empty((B, H, n_rows, D_v), dtype=np.float64)
+    lse = np.empty((B, H, n_rows), dtype=np.float64)
+    p = np.empty((B, H, n_rows, S_k), dtype=np.float64) if want_probs else None
+    lib = lib or _library()
+    rc = lib.attn_ref_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(p),
+                          B, H, S_q, S_k, D_qk, D_v, float(scale), int(bool(causal)),
+                          rows_p, n_rows, int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"attn_ref_f64 failed with status {rc}")
+    return (o, lse, p) if want_probs else (o, lse)

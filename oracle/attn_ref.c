@@ -1,0 +1,200 @@
+/*
+ * fp64 CPU oracle for scaled dot-product attention (forward).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header or constant with the
+ * GPU library.
+ *
+ * What it computes (the plain, non-online definition):
+ *   VeriTile, "FlashAttention1.NaiveRefinement", section "Naive FA reference":
+ *   `fa1NaiveReference4D` = `attentionReal4D`, i.e. softmax(Q K^T * scale) V
+ *   for every (batch, head) slice, output indexed like Q; and
+ *   `fa1NaiveCausalReference4D` = `attentionReal4DCausal`, its causal form.
+ *   The same page's refinement theorems state that the tiled FA-1 kernels
+ *   (non-causal and causal, with S_q / S_k boundaries and a head-dim tail)
+ *   equal these references exactly in real arithmetic, so the oracle is the
+ *   reference itself, evaluated in double precision.
+ *
+ * Order of operations per query row, as the reductions are chained on
+ *   tiny.accy.kernel.library.attention (the `reductions` list of the
+ *   scaled-dot-product specialization, and the test helper `expectedOutput`):
+ *     1. score_dot       s_j = scale * sum_d Q[i,d] K[j,d]   (dot first, then scale)
+ *     2. score_max       m   = max_j s_j, starting from -infinity
+ *     3. score_exp_sum   l   = sum_j exp(s_j - m)
+ *     4. weighted_sum    O[i,e] = sum_j (exp(s_j - m) / l) * V[j,e]
+ *                        (the weight is formed first, then multiplied)
+ *   plus LSE[i] = m + ln(l)  (natural log of the sum of exp of scaled scores).
+ *   The key width D_qk may differ from the value width D_v (equation
+ *   "bqh,bkh,bkv->bqv" on the same page).
+ *
+ * Readings where the pages are silent (each listed in the design notes):
+ *   - causal: key j is visible to query i iff j <= i (top-left alignment);
+ *     rows i >= S_k therefore see every key;
+ *   - masked keys are simply left out of every sum (exact);
+ *   - LSE uses the natural logarithm of the scaled scores.
+ *
+ * Layout: contiguous row-major Q[B,H,S_q,D_qk], K[B,H,S_k,D_qk],
+ * V[B,H,S_k,D_v], O[B,H,S_q,D_v], LSE[B,H,S_q] (all double).
+ * With a row list, only those query rows are computed and O / LSE are
+ * packed as [B,H,n_rows,D_v] / [B,H,n_rows].
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+typedef struct {
+    const double *Q, *K, *V;
+    double *O, *LSE, *P;
+    int64_t B, H, S_q, S_k, D_qk, D_v;
+    double scale;
+    int causal;
+    const int64_t *rows;
+    int64_t n_rows;          /* rows computed per slice */
+    int64_t first, last;     /* work items [first, last) over slices*n_rows */
+    int status;
+} oracle_job;
+
+/* One query row of one (batch, head) slice. */
+static void oracle_row(const oracle_job *jb, int64_t slice, int64_t out_row,
+                       int64_t i, double *s, double *w, double *acc)
+{
+    const double *q = jb->Q + (slice * jb->S_q + i) * jb->D_qk;
+    const double *k = jb->K + slice * jb->S_k * jb->D_qk;
+    const double *v = jb->V + slice * jb->S_k * jb->D_v;
+
+    /* valid keys: all of them, or j <= i when causal */
+    int64_t n_valid = jb->S_k;
+    if (jb->causal && i + 1 < n_valid)
+        n_valid = i + 1;
+
+    /* 1. score_dot, then the scale */
+    for (int64_t j = 0; j < n_valid; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < jb->D_qk; ++d)
+            dot += q[d] * k[j * jb->D_qk + d];
+        s[j] = jb->scale * dot;
+    }
+    /* 2. score_max, seeded with -infinity */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n_valid; ++j)
+        if (s[j] > m)
+            m = s[j];
+    /* 3. score_exp_sum: the shifted exponentials summed */
+    double l = 0.0;
+    for (int64_t j = 0; j < n_valid; ++j)
+        l += exp(s[j] - m);
+    /* 4. weighted_sum: weight = exp(s_j - m) / l, then weight * V[j, e] */
+    for (int64_t j = 0; j < n_valid; ++j)
+        w[j] = exp(s[j] - m) / l;
+    for (int64_t e = 0; e < jb->D_v; ++e)
+        acc[e] = 0.0;
+    for (int64_t j = 0; j < n_valid; ++j)
+        for (int64_t e = 0; e < jb->D_v; ++e)
+            acc[e] += w[j] * v[j * jb->D_v + e];
+
+    double *o = jb->O + (slice * jb->n_rows + out_row) * jb->D_v;
+    for (int64_t e = 0; e < jb->D_v; ++e)
+        o[e] = acc[e];
+    if (jb->LSE)
+        jb->LSE[slice * jb->n_rows + out_row] = m + log(l);
+    if (jb->P) {
+        double *p = jb->P + (slice * jb->n_rows + out_row) * jb->S_k;
+        for (int64_t j = 0; j < jb->S_k; ++j)
+            p[j] = j < n_valid ? w[j] : 0.0;
+    }
+}
+
+static void *oracle_worker(void *arg)
+{
+    oracle_job *jb = (oracle_job *)arg;
+    double *s = (double *)malloc(sizeof(double) * (size_t)jb->S_k);
+    double *w = (double *)malloc(sizeof(double) * (size_t)jb->S_k);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)jb->D_v);
+    if (!s || !w || !acc) {
+        jb->status = 3;
+    } else {
+        for (int64_t it = jb->first; it < jb->last; ++it) {
+            int64_t slice = it / jb->n_rows;
+            int64_t r = it % jb->n_rows;
+            int64_t i = jb->rows ? jb->rows[r] : r;
+            oracle_row(jb, slice, r, i, s, w, acc);
+        }
+    }
+    free(s);
+    free(w);
+    free(acc);
+    return NULL;
+}
+
+/*
+ * Returns 0 on success, 1 for a bad argument (null pointer, a dimension
+ * below 1, a row index outside [0, S_q)), 2 if a thread could not be
+ * started, 3 if a work buffer could not be allocated.
+ * P, when not NULL, receives the softmax weights [B,H,rows,S_k] (0 where a
+ * key is masked); LSE may be NULL.
+ */
+int attn_ref_f64(const double *Q, const double *K, const double *V,
+                 double *O, double *LSE, double *P,
+                 int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                 int64_t D_qk, int64_t D_v, double scale, int causal,
+                 const int64_t *rows, int64_t n_rows, int nthreads)
+{
+    if (!Q || !K || !V || !O)
+        return 1;
+    if (B < 1 || H < 1 || S_q < 1 || S_k < 1 || D_qk < 1 || D_v < 1)
+        return 1;
+    if (rows) {
+        if (n_rows < 1)
+            return 1;
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (rows[r] < 0 || rows[r] >= S_q)
+                return 1;
+    } else {
+        n_rows = S_q;
+    }
+    int64_t total = B * H * n_rows;
+    if (nthreads < 1)
+        nthreads = 1;
+    if ((int64_t)nthreads > total)
+        nthreads = (int)total;
+
+    oracle_job *jobs = (oracle_job *)calloc((size_t)nthreads, sizeof(oracle_job));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return 3;
+    }
+    int rc = 0, started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        oracle_job *jb = &jobs[t];
+        jb->Q = Q; jb->K = K; jb->V = V;
+        jb->O = O; jb->LSE = LSE; jb->P = P;
+        jb->B = B; jb->H = H; jb->S_q = S_q; jb->S_k = S_k;
+        jb->D_qk = D_qk; jb->D_v = D_v;
+        jb->scale = scale; jb->causal = causal;
+        jb->rows = rows; jb->n_rows = n_rows;
+        jb->first = total * t / nthreads;
+        jb->last = total * (t + 1) / nthreads;
+        jb->status = 0;
+    }
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, oracle_worker, &jobs[t]) != 0) {
+            rc = 2;
+            break;
+        }
+        started = t;
+    }
+    if (rc == 0)
+        oracle_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(tids[t], NULL);
+    for (int t = 0; t < nthreads && rc == 0; ++t)
+        if (jobs[t].status)
+            rc = jobs[t].status;
+    free(jobs);
+    free(tids);
+    return rc;
+}
