@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark: attention forward TFLOP/s and fraction of the MFMA peak.
+
+One step = one forward pass (attn_fwd) over the whole workload, inputs
+already resident in HBM.  Default workload: bf16, causal, B=1, H=32,
+S_q=S_k=16384, D_qk=D_v=128 (the headline configuration).
+
+Prints ONE JSON line.  FLOPs per step follow the metric's count:
+2*B*H*S_q*S_k*(D_qk+D_v), halved for causal.  `roofline.achieved` divides
+that count by the kernel's average launch duration, timed with HIP events
+recorded on the stream the kernel runs on (torch's current stream, which is
+the stream the binding passes to the library).  `cpu_baseline` times the
+fp64 CPU oracle on a bounded row sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# Published MI355X dense peaks (TFLOP/s) by compute dtype, and HBM bandwidth.
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "tiled_scaled_dot_amd", "csrc", "attn_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None, help="workload name (default: headline)")
+    ap.add_argument("--cpu-row-stride", type=int, default=2,
+                    help="oracle sample: every N-th query row of every head")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, stride: int):
+    import numpy as np
+
+    import oracle
+
+    rows = list(range(stride - 1, w.S_q, stride))
+    qd = q.double().numpy()
+    kd = k.double().numpy()
+    vd = v.double().numpy()
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.attn_ref(qd, kd, vd, w.scale, w.causal, rows=rows, nthreads=threads)
+    dt = time.perf_counter() - t0
+    pairs = sum((min(r + 1, w.S_k) if w.causal else w.S_k) for r in rows) * w.B * w.H
+    flops = 2.0 * pairs * (w.D_qk + w.D_v)
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"query rows i = {stride - 1} mod {stride} of all {w.B * w.H} slices "
+                   f"({len(rows)} rows/slice, {flops / 1e9:.1f} GFLOP of visible pairs, "
+                   f"{dt:.1f} s, fp64, {cpu_model or platform.processor()})"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards per (batch, head) slice with no exchange, but no multi-GPU "
+              "run is part of it.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import tiled_scaled_dot_amd as tsd
+    from tiled_scaled_dot_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    q, k, v = make_inputs(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    o = torch.empty(w.shape_o, dtype=qd.dtype, device=dev)
+    lse = torch.empty((w.B, w.H, w.S_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        tsd.attn_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    flops = w.metric_flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = stored_traffic(name)
+
+    result = {
+        "metric": "attention fwd TFLOP/s and % of MFMA peak (bf16 causal, S=16k, D=128)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": name,
+            "B": w.B, "H": w.H, "S_q": w.S_q, "S_k": w.S_k, "D_qk": w.D_qk, "D_v": w.D_v,
+            "causal": w.causal, "scale": w.scale,
+            "inputs": (f"{w.dist} Q,K sigma={w.sigma_qk:.4g}, V sigma={w.sigma_v:.4g}, "
+                       f"seed {w.seed}" if w.dist == "normal" else f"{w.dist}(-1,1), seed {w.seed}"),
+            "flops_per_step": flops,
+            "pct_of_mfma_peak": round(100.0 * achieved / peak, 2),
+            "device": torch.cuda.get_device_name(dev),
+            "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+            "kernel_ms": round(kernel_ms, 4),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        del qd, kd, vd, o, lse
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_row_stride)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

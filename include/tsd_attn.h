@@ -1,0 +1,126 @@
+/*
+ * tsd_attn.h — C ABI of the MI355X (gfx950) tiled scaled-dot-product
+ * attention forward library (libtsd_attn.so).
+ *
+ * Operation (VeriTile, "FlashAttention1.NaiveRefinement": the definitions
+ * `fa1NaiveReference4D` / `fa1NaiveCausalReference4D` and the refinement
+ * theorems for the FA-1 boundary + head-dim-tail kernels):
+ *
+ *   for every batch b < B, head h < H, query row i < S_q:
+ *     s_j      = scale * sum_{d < D_qk} Q[b,h,i,d] * K[b,h,j,d]
+ *     O[b,h,i,e] = sum_j softmax_j(s) * V[b,h,j,e]          (e < D_v)
+ *     LSE[b,h,i] = ln sum_j exp(s_j)
+ *   where j runs over 0 .. S_k-1, or over 0 .. min(i, S_k-1) when causal
+ *   (key j visible to query i iff j <= i, top-left alignment).
+ *
+ * The key/query width D_qk may differ from the value width D_v (equation
+ * "bqh,bkh,bkv->bqv", tiny.accy.kernel.library.attention).  The result is
+ * computed tile by tile with an online softmax (running row max and sum);
+ * in real arithmetic that equals the plain definition above exactly.
+ */
+#ifndef TSD_ATTN_H
+#define TSD_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every check runs on the host before any HIP call; on an
+ * error nothing is launched and no output byte is written. */
+enum {
+    TSD_OK = 0,
+    TSD_ERR_NULL = 1,        /* Q, K, V or O is NULL (or plan output NULL)      */
+    TSD_ERR_SHAPE = 2,       /* a dimension below 1 (the refinement theorems
+                                require 0 < S_k; empty inputs are rejected)    */
+    TSD_ERR_UNSUPPORTED = 3, /* D_qk or D_v above 128 (the block width: the
+                                theorems need D <= block width), an unknown
+                                dtype, a misaligned pointer, or a size beyond
+                                the 32-bit in-slice / grid limits               */
+    TSD_ERR_SCALE = 4,       /* scale is NaN or infinite                        */
+    TSD_ERR_ALIAS = 5,       /* O or LSE overlaps Q, K, V, or each other (the
+                                output region must be disjoint from the inputs) */
+    TSD_ERR_HIP = 6          /* the kernel launch itself failed                 */
+};
+
+/* Storage dtypes of Q, K, V and O (all four share one).  Accumulation is
+ * always f32; LSE is always f32. */
+enum {
+    TSD_F32 = 0,
+    TSD_F16 = 1,
+    TSD_BF16 = 2
+};
+
+/* Launch plan, as chosen by the planner for one call (pure host data). */
+typedef struct tsd_plan {
+    int32_t dtype;          /* TSD_F32 / TSD_F16 / TSD_BF16                     */
+    int32_t causal;         /* 0 or 1                                           */
+    int32_t block_m;        /* query rows per workgroup                         */
+    int32_t block_n;        /* keys per K/V tile                                */
+    int32_t dqk_block;      /* padded Q/K width the kernel runs at (>= D_qk)    */
+    int32_t dv_block;       /* padded V/O width the kernel runs at (>= D_v)     */
+    int32_t waves;          /* 64-lane waves per workgroup                      */
+    int32_t threads;        /* threads per workgroup                            */
+    int32_t lds_bytes;      /* LDS per workgroup                                */
+    int32_t order;          /* 0: slice-major order; 1: slices grouped per XCD  */
+    int64_t slices;         /* B * H                                            */
+    int64_t q_blocks;       /* query blocks per slice = ceil(S_q / block_m)     */
+    int64_t kv_blocks;      /* key tiles per slice    = ceil(S_k / block_n)     */
+    int64_t grid;           /* workgroups launched = q_blocks * slices          */
+    int64_t total_kv_steps; /* sum over workgroups of the key tiles visited     */
+    int64_t vector_io;      /* 1: 16-byte global loads/stores; 0: per element   */
+} tsd_plan;
+
+/*
+ * attn_fwd — enqueue the forward pass on `stream` and return.
+ *
+ *   Q   [B,H,S_q,D_qk], K [B,H,S_k,D_qk], V [B,H,S_k,D_v], O [B,H,S_q,D_v]:
+ *       contiguous row-major device buffers of `dtype` (TSD_F32/F16/BF16),
+ *       each aligned to its element size.
+ *   LSE [B,H,S_q] contiguous f32 device buffer, natural log of the softmax
+ *       denominator of the scaled scores; may be NULL (then not written).
+ *   scale  any finite float (0 and negative allowed); multiplies the dot
+ *       product.
+ *   causal 0 or nonzero (top-left: key j visible to query i iff j <= i).
+ *   stream a hipStream_t (NULL = the null stream).
+ *
+ * Ownership: the caller allocates and frees every buffer; the library
+ * allocates no device memory, keeps no pointer after returning, and never
+ * synchronises.  It holds no global state and may be called from several
+ * threads.  Only rows i < S_q and columns e < D_v of O, and only the B*H*S_q
+ * entries of LSE, are written.  Returns a TSD_* status.
+ */
+int attn_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
+             int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+             int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+             void *stream);
+
+/*
+ * attn_fwd_plan — fill `out` with the plan attn_fwd would use for these
+ * sizes (no HIP call, no device access).  Pointer alignment is not known
+ * here, so `vector_io` reports what aligned buffers would get.  Returns the
+ * same shape/dtype statuses as attn_fwd (TSD_ERR_NULL if out is NULL).
+ */
+int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                  int64_t D_qk, int64_t D_v, int causal, int dtype,
+                  tsd_plan *out);
+
+/*
+ * attn_fwd_plan_block — for workgroup `block` (0 <= block < plan->grid),
+ * report the query block, the (batch*H + head) slice and the number of key
+ * tiles it visits, exactly as the kernel derives them (host only).
+ * Returns TSD_ERR_SHAPE if `block` is out of range.
+ */
+int attn_fwd_plan_block(const tsd_plan *plan, int64_t S_q, int64_t S_k,
+                        int64_t block, int64_t *q_block, int64_t *slice,
+                        int64_t *kv_steps);
+
+/* attn_status_string — static text for a status code (never NULL). */
+const char *attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TSD_ATTN_H */

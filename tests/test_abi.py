@@ -1,0 +1,205 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* the library loads and exports every function include/tsd_attn.h declares;
+* every invalid call returns its status before any HIP call (fake device
+  addresses are never dereferenced because nothing is launched);
+* the planner: grid, key-tile counts, causal work, heaviest-first order,
+  XCD grouping, and exactly-once coverage of every (query block, slice).
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_scaled_dot_amd as tsd
+from tiled_scaled_dot_amd.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tsd_attn.h")
+
+pytestmark = pytest.mark.cpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(tsd.LIBRARY_PATH):
+        from tiled_scaled_dot_amd import build
+        build.build()
+    return tsd.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(tsd.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", tsd.LIBRARY_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\w+)$", out, flags=re.M))
+    for name in declared_functions():
+        assert name in exported, f"{name} not exported"
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert tsd.attn_status_string(code)
+    assert tsd.attn_status_string(99) == "unknown status"
+
+
+# Fake, 256-byte aligned, non-overlapping device addresses: every call below
+# must be rejected on the host, so none is ever dereferenced.
+QA, KA, VA, OA, LA = (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000)
+GOOD = dict(B=1, H=2, S_q=128, S_k=128, D_qk=64, D_v=64)
+
+
+def call(q=QA, k=KA, v=VA, o=OA, lse=LA, scale=0.125, causal=0, dtype=2, **dims):
+    d = dict(GOOD)
+    d.update(dims)
+    return tsd.attn_fwd_raw(q, k, v, o, lse, d["B"], d["H"], d["S_q"], d["S_k"], d["D_qk"],
+                            d["D_v"], scale, causal, dtype)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_null_pointer(lib, which):
+    assert call(**{which: None}) == 1
+
+
+@pytest.mark.parametrize("dim", ["B", "H", "S_q", "S_k", "D_qk", "D_v"])
+@pytest.mark.parametrize("value", [0, -1])
+def test_bad_shape(lib, dim, value):
+    assert call(**{dim: value}) == 2
+
+
+@pytest.mark.parametrize("dims", [dict(D_qk=129), dict(D_v=129), dict(D_qk=256, D_v=256)])
+def test_head_dim_above_block_width(lib, dims):
+    assert call(**dims) == 3
+
+
+@pytest.mark.parametrize("dtype", [-1, 3, 7])
+def test_unknown_dtype(lib, dtype):
+    assert call(dtype=dtype) == 3
+
+
+def test_slice_too_large(lib):
+    # a single slice of 2^31 bytes or more is rejected (32-bit in-slice offsets)
+    assert call(S_q=(1 << 24), D_qk=128, dtype=0) == 3
+    assert call(S_k=(1 << 24), D_v=128, dtype=0) == 3
+
+
+def test_misaligned(lib):
+    assert call(q=QA + 1) == 3          # not element aligned (bf16)
+    assert call(o=OA + 2, dtype=0) == 3  # not element aligned (f32)
+    assert call(lse=LA + 2) == 3
+
+
+@pytest.mark.parametrize("scale", [float("nan"), float("inf"), float("-inf")])
+def test_scale_not_finite(lib, scale):
+    assert call(scale=scale) == 4
+
+
+@pytest.mark.parametrize("o,lse", [(QA, LA), (KA + 64, LA), (VA - 4096, LA),
+                                   (OA, QA + 8), (OA, OA + 100), (OA, VA)])
+def test_aliasing(lib, o, lse):
+    assert call(o=o, lse=lse) == 5
+
+
+def test_output_adjacent_is_not_alias(lib):
+    # O ends exactly where LSE begins: no overlap, so the call passes validation
+    # and would launch; only the plan is checked here.
+    o_bytes = 1 * 2 * 128 * 64 * 2
+    plan = tsd.attn_fwd_plan(1, 2, 128, 128, 64, 64, False, "bf16")
+    assert plan.grid == 2
+    assert OA + o_bytes <= LA
+
+
+def test_plan_errors(lib):
+    with pytest.raises(tsd.TsdError) as e:
+        tsd.attn_fwd_plan(1, 1, 0, 4, 64, 64)
+    assert e.value.status == 2
+    with pytest.raises(tsd.TsdError) as e:
+        tsd.attn_fwd_plan(1, 1, 4, 4, 200, 64)
+    assert e.value.status == 3
+    assert lib.attn_fwd_plan(1, 1, 4, 4, 8, 8, 0, 2, None) == 1
+
+
+# ------------------------------------------------------------------ planner
+def expected_tiles(qb, bm, bn, S_q, S_k, causal):
+    if not causal:
+        return math.ceil(S_k / bn)
+    last_q = min((qb + 1) * bm, S_q) - 1
+    return math.ceil(min(last_q + 1, S_k) / bn)
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_plan_for_workloads(lib, name):
+    w = WORKLOADS[name]
+    plan = tsd.attn_fwd_plan(w.B, w.H, w.S_q, w.S_k, w.D_qk, w.D_v, w.causal, w.dtype)
+    assert plan.block_m == 128 and plan.threads == 256 and plan.waves == 4
+    assert plan.block_n == (32 if w.dtype == "f32" else 64)
+    assert plan.dqk_block >= w.D_qk and plan.dv_block >= w.D_v
+    assert plan.lds_bytes <= 64 * 1024
+    assert plan.slices == w.B * w.H
+    assert plan.q_blocks == math.ceil(w.S_q / 128)
+    assert plan.kv_blocks == math.ceil(w.S_k / plan.block_n)
+    assert plan.grid == plan.q_blocks * plan.slices
+    assert plan.order == (1 if plan.slices % 8 == 0 else 0)
+    total = sum(expected_tiles(qb, 128, plan.block_n, w.S_q, w.S_k, w.causal)
+                for qb in range(plan.q_blocks)) * plan.slices
+    assert plan.total_kv_steps == total
+
+
+@pytest.mark.parametrize("B,H,S_q,S_k,causal", [
+    (1, 2, 128, 128, False), (2, 4, 1000, 777, True), (2, 4, 1000, 777, False),
+    (1, 8, 700, 300, True), (3, 5, 513, 1029, True), (2, 8, 1024, 1024, True),
+    (1, 32, 2048, 2048, True), (1, 1, 1, 1, True),
+])
+def test_block_map_covers_each_tile_once(lib, B, H, S_q, S_k, causal):
+    plan = tsd.attn_fwd_plan(B, H, S_q, S_k, 128, 128, causal, "bf16")
+    seen = set()
+    steps_in_order = []
+    for blk in range(plan.grid):
+        qb, sl, steps = tsd.attn_fwd_plan_block(plan, S_q, S_k, blk)
+        assert 0 <= qb < plan.q_blocks and 0 <= sl < plan.slices
+        assert steps == expected_tiles(qb, 128, plan.block_n, S_q, S_k, causal)
+        seen.add((qb, sl))
+        steps_in_order.append(steps)
+        if plan.order == 1:
+            # every workgroup of a slice lands on the same XCD (id % 8)
+            assert sl % 8 == blk % 8
+    assert len(seen) == plan.grid
+    assert sum(steps_in_order) == plan.total_kv_steps
+    if causal:
+        # heaviest first: the work per workgroup never grows along the launch order
+        assert all(a >= b for a, b in zip(steps_in_order, steps_in_order[1:]))
+    with pytest.raises(tsd.TsdError):
+        tsd.attn_fwd_plan_block(plan, S_q, S_k, plan.grid)
+
+
+def test_vector_io_flag(lib):
+    assert tsd.attn_fwd_plan(1, 1, 64, 64, 80, 80, False, "f32").vector_io == 1
+    assert tsd.attn_fwd_plan(1, 1, 64, 64, 80, 80, False, "bf16").vector_io == 1
+    assert tsd.attn_fwd_plan(1, 1, 64, 64, 33, 64, False, "bf16").vector_io == 0
+    assert tsd.attn_fwd_plan(1, 1, 64, 64, 64, 6, False, "f32").vector_io == 0
+
+
+def test_product_code_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "tiled_scaled_dot_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, flags=re.M), f
+                assert "liboracle" not in text and "attn_ref" not in text, f
+    hdr = open(HEADER).read()
+    assert "oracle" not in hdr.lower()

@@ -1,1 +1,171 @@
-"""MI355X-native tiled scaled-dot-product attention forward (gfx950)."""
+"""MI355X-native (gfx950) tiled scaled-dot-product attention forward.
+
+Thin ctypes binding over ``libtsd_attn.so`` (C ABI in ``include/tsd_attn.h``).
+This module only marshals arguments: every step of the computation runs in
+the library's HIP kernels.  PyTorch supplies device memory and streams.
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string",
+           "TsdError", "library", "LIBRARY_PATH", "DTYPE_CODES", "STATUS"]
+
+LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsd_attn.so")
+
+STATUS = {
+    0: "TSD_OK",
+    1: "TSD_ERR_NULL",
+    2: "TSD_ERR_SHAPE",
+    3: "TSD_ERR_UNSUPPORTED",
+    4: "TSD_ERR_SCALE",
+    5: "TSD_ERR_ALIAS",
+    6: "TSD_ERR_HIP",
+}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+EXPORTED = ("attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string")
+
+
+class TsdError(RuntimeError):
+    def __init__(self, status: int, text: str):
+        super().__init__(f"{STATUS.get(status, status)}: {text}")
+        self.status = status
+
+
+class TsdPlan(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("block_m", ctypes.c_int32),
+        ("block_n", ctypes.c_int32),
+        ("dqk_block", ctypes.c_int32),
+        ("dv_block", ctypes.c_int32),
+        ("waves", ctypes.c_int32),
+        ("threads", ctypes.c_int32),
+        ("lds_bytes", ctypes.c_int32),
+        ("order", ctypes.c_int32),
+        ("slices", ctypes.c_int64),
+        ("q_blocks", ctypes.c_int64),
+        ("kv_blocks", ctypes.c_int64),
+        ("grid", ctypes.c_int64),
+        ("total_kv_steps", ctypes.c_int64),
+        ("vector_io", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
+    """Load libtsd_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m tiled_scaled_dot_amd.build` (there is no fallback)")
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                             ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd_plan.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.POINTER(TsdPlan)]
+    lib.attn_fwd_plan.restype = ctypes.c_int
+    lib.attn_fwd_plan_block.argtypes = [ctypes.POINTER(TsdPlan), i64, i64, i64,
+                                        ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                        ctypes.POINTER(i64)]
+    lib.attn_fwd_plan_block.restype = ctypes.c_int
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return library().attn_status_string(int(status)).decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise TsdError(status, attn_status_string(status))
+
+
+def attn_fwd_plan(B, H, S_q, S_k, D_qk, D_v, causal=False, dtype="bf16") -> TsdPlan:
+    plan = TsdPlan()
+    code = DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+    _check(library().attn_fwd_plan(B, H, S_q, S_k, D_qk, D_v, int(bool(causal)), code,
+                                   ctypes.byref(plan)))
+    return plan
+
+
+def attn_fwd_plan_block(plan: TsdPlan, S_q: int, S_k: int, block: int):
+    """(query block, slice, key tiles visited) of workgroup `block`."""
+    qb, sl, steps = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(library().attn_fwd_plan_block(ctypes.byref(plan), S_q, S_k, block, ctypes.byref(qb),
+                                         ctypes.byref(sl), ctypes.byref(steps)))
+    return qb.value, sl.value, steps.value
+
+
+def attn_fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk, D_v, scale,
+                 causal, dtype, stream=None) -> int:
+    """Direct call with integer device addresses; returns the TSD status."""
+    code = DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+    return library().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk, D_v,
+                              float(scale), int(bool(causal)), code, stream)
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):
+    """O, LSE = softmax(q k^T * scale) v  (per batch and head).
+
+    q [B,H,S_q,D_qk], k [B,H,S_k,D_qk], v [B,H,S_k,D_v]: contiguous CUDA
+    tensors of one dtype (float32, float16 or bfloat16).  ``scale`` defaults
+    to 1/sqrt(D_qk).  Returns O [B,H,S_q,D_v] (input dtype) and LSE
+    [B,H,S_q] (float32).  Runs on ``stream`` (default: torch's current
+    stream) and does not synchronise.
+    """
+    import torch
+
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if q.dtype not in codes or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype among float32, float16, bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B,H,S,D]")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, S_q, D_qk = q.shape
+    S_k, D_v = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, H, S_k, D_qk) or tuple(v.shape) != (B, H, S_k, D_v):
+        raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} "
+                         f"v{tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_qk)
+    if out is None:
+        out = torch.empty((B, H, S_q, D_v), dtype=q.dtype, device=q.device)
+    elif (tuple(out.shape) != (B, H, S_q, D_v) or out.dtype != q.dtype
+          or not out.is_contiguous() or out.device != q.device):
+        raise ValueError("out must be a contiguous [B,H,S_q,D_v] tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, S_q), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (B, H, S_q) or lse.dtype != torch.float32
+          or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B,H,S_q] tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    status = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                          lse.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal,
+                          codes[q.dtype], stream)
+    _check(status)
+    return out, lse

@@ -1,0 +1,667 @@
+// gfx950 (CDNA4) kernels for the tiled scaled-dot-product attention forward.
+//
+// What is computed: O = softmax(Q K^T * scale) V and LSE = ln(sum exp) per
+// (batch, head) slice, non-causal or causal, with S_q / S_k boundaries and a
+// head-dim tail (VeriTile, "FlashAttention1.NaiveRefinement": the FA-1
+// boundary + D-tail kernels refine the naive reference).  Each query row
+// runs the reduction chain dot -> max -> shifted exp-sum -> weighted sum
+// (tiny.accy.kernel.library.attention, the specialization's reductions),
+// online over key tiles: the running max m and sum l are rescaled by
+// exp(m_old - m_new) whenever m grows, which in real arithmetic gives the
+// plain definition exactly.
+//
+// Work decomposition (one workgroup = one query block of one slice):
+//   * 4 waves x 32 query rows = 128 rows per workgroup.
+//   * Each wave keeps its 32 query rows in VGPRs for the whole key loop.
+//   * Key/value tiles are staged through LDS, double buffered: the global
+//     loads of tile t+1 are in flight while tile t is computed.
+//   * Scores are formed transposed, S^T = K Q^T, on MFMA: the 32x32 result
+//     puts one query per lane column, so each lane holds 16 keys of a single
+//     query and the row max / sum are in-lane plus one swap with lane^32.
+//   * The S^T accumulator layout is exactly the B operand layout of the
+//     P V MFMA (O^T = V^T P^T), so P never leaves registers.  V is written
+//     to LDS transposed (d-major) so the A operand reads 8 contiguous keys.
+//   * Key rows read for the score MFMA are permuted (sigma below) so that
+//     each lane's P values cover 8 consecutive keys, which makes every LDS
+//     operand read a single 16-byte access.  Permuting keys is legal: the
+//     key index is only summed over.
+//   * 16-bit inputs: v_mfma_f32_32x32x16_{bf16,f16}; f32 inputs:
+//     v_mfma_f32_32x32x2_f32.  Accumulation is always f32.
+//   * exp is computed as exp2 with log2(e) folded into the scale.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace tsd {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kBlockM = 128;    // 4 waves x 32 query rows
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ inline float neg_inf() { return -__builtin_inff(); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Swap-half reduction partner: lane l <-> lane l ^ 32.
+__device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
+
+// ---------------------------------------------------------------- MFMA
+template <bool BF16>
+__device__ inline f32x16 mma16(u32x4 a, u32x4 b, f32x16 c)
+{
+    if constexpr (BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ inline f32x16 mma32(float a, float b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Two f32 -> one word of two 16-bit values (round to nearest even).
+template <bool BF16>
+__device__ inline uint32_t pack2(float lo, float hi)
+{
+    if constexpr (BF16) {
+        bf16x2 v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        f16x2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+// ------------------------------------------------------- layout helpers
+// MFMA 32x32 accumulator: lane l, register r holds row (r/4)*8 + 4*(l/32) + r%4
+// and column l%32.  For the score MFMA the row is a key; sigma maps the MFMA
+// row i to the key of the tile read into it so that lane half h, registers
+// 8u..8u+7 hold keys 16u + 8h + 0..7.
+__device__ inline int sigma(int i)
+{
+    return (i & 16) | (((i >> 2) & 1) << 3) | (((i >> 3) & 1) << 2) | (i & 3);
+}
+
+// XOR swizzle of 16-byte chunks within a row (LDS bank spreading).  For
+// ds_read_b128 every group of 8 lanes must hit 8 different 16-byte bank
+// groups; the reads here visit rows {sigma(0..7)}, {sigma(8..15)}, ... and
+// the transposed-V writes visit rows {e, e+4, ..., e+28}; this XOR makes
+// both patterns conflict-free.
+__device__ inline int swz(int row)
+{
+    return (((row & 3) | ((row >> 1) & 4)) ^ ((row >> 2) & 7));
+}
+
+// ====================================================================
+// 16-bit (bf16 / f16) kernel
+// ====================================================================
+template <int DQ, int DV>
+struct Tile16 {
+    static constexpr int BN = 64;                   // keys per tile
+    static constexpr int KCH = DQ / 8;              // 16-byte chunks per K row
+    static constexpr int VCH = BN / 8;              // 16-byte chunks per V^T row
+    static constexpr int K_CHUNKS = BN * KCH;
+    static constexpr int V_CHUNKS = DV * VCH;
+    static constexpr int STAGE = K_CHUNKS + V_CHUNKS;   // chunks per LDS stage
+    static constexpr int K_PER_T = K_CHUNKS / kThreads; // K chunks loaded per thread
+    static constexpr int V_UNITS = (BN / 8) * (DV / 4); // (8 keys x 4 dims) units
+    static constexpr int V_PER_T = (V_UNITS + kThreads - 1) / kThreads;
+    static_assert(K_CHUNKS % kThreads == 0, "K tile must split evenly");
+};
+
+template <int DQ, int DV>
+struct Regs16 {
+    u32x4 k[Tile16<DQ, DV>::K_PER_T];
+    u32x2 v[Tile16<DQ, DV>::V_PER_T][8];
+};
+
+template <int DQ, int DV>
+__device__ inline void load_tile16(Regs16<DQ, DV> &r, const uint16_t *__restrict__ Ks,
+                                   const uint16_t *__restrict__ Vs, int kbase,
+                                   const KernelArgs &p, int tid)
+{
+    using T = Tile16<DQ, DV>;
+#pragma unroll
+    for (int it = 0; it < T::K_PER_T; ++it) {
+        const int ci = tid + kThreads * it;
+        const int row = ci / T::KCH, c = ci % T::KCH;
+        const int key = kbase + row;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (p.vec) {
+            if (key < p.S_k && c * 8 < p.D_qk)
+                x = *reinterpret_cast<const u32x4 *>(Ks + (size_t)key * p.D_qk + c * 8);
+        } else if (key < p.S_k) {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int d = c * 8 + 2 * e;
+                const uint32_t lo = d < p.D_qk ? Ks[(size_t)key * p.D_qk + d] : 0u;
+                const uint32_t hi = d + 1 < p.D_qk ? Ks[(size_t)key * p.D_qk + d + 1] : 0u;
+                w[e] = lo | (hi << 16);
+            }
+            x = u32x4{w[0], w[1], w[2], w[3]};
+        }
+        r.k[it] = x;
+    }
+#pragma unroll
+    for (int it = 0; it < T::V_PER_T; ++it) {
+        const int u = tid + kThreads * it;
+        const int kg = u / (DV / 4), dq = u % (DV / 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int key = kbase + kg * 8 + j;
+            const int d0 = dq * 4;
+            u32x2 x = {0u, 0u};
+            if (u < T::V_UNITS && key < p.S_k) {
+                if (p.vec) {
+                    if (d0 < p.D_v)
+                        x = *reinterpret_cast<const u32x2 *>(Vs + (size_t)key * p.D_v + d0);
+                } else {
+                    uint32_t e4[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        e4[e] = d0 + e < p.D_v ? Vs[(size_t)key * p.D_v + d0 + e] : 0u;
+                    x = u32x2{e4[0] | (e4[1] << 16), e4[2] | (e4[3] << 16)};
+                }
+            }
+            r.v[it][j] = x;
+        }
+    }
+}
+
+template <int DQ, int DV>
+__device__ inline void store_tile16(const Regs16<DQ, DV> &r, u32x4 *__restrict__ stage, int tid)
+{
+    using T = Tile16<DQ, DV>;
+#pragma unroll
+    for (int it = 0; it < T::K_PER_T; ++it) {
+        const int ci = tid + kThreads * it;
+        const int row = ci / T::KCH, c = ci % T::KCH;
+        stage[row * T::KCH + (c ^ swz(row))] = r.k[it];
+    }
+    u32x4 *vt = stage + T::K_CHUNKS;
+#pragma unroll
+    for (int it = 0; it < T::V_PER_T; ++it) {
+        const int u = tid + kThreads * it;
+        if (u < T::V_UNITS) {
+            const int kg = u / (DV / 4), dq = u % (DV / 4);
+            // r.v[it][j] holds dims 4dq..4dq+3 of key 8kg+j; V^T row 4dq+e
+            // takes element e of each of the 8 keys.
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t w[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const uint32_t a = (e < 2) ? r.v[it][2 * m].x : r.v[it][2 * m].y;
+                    const uint32_t b = (e < 2) ? r.v[it][2 * m + 1].x : r.v[it][2 * m + 1].y;
+                    w[m] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u))
+                                   : ((a & 0xffffu) | (b << 16));
+                }
+                const int d = dq * 4 + e;
+                vt[d * T::VCH + (kg ^ swz(d))] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+    }
+}
+
+template <int DQ, int DV, bool CAUSAL, bool BF16>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+attn_fwd_16(KernelArgs p)
+{
+    using T = Tile16<DQ, DV>;
+    constexpr int BN = T::BN;
+    __shared__ u32x4 lds[2 * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, l32 = lane & 31;
+
+    int32_t qb, slice;
+    map_block((int32_t)blockIdx.x, p.q_blocks, p.slices, p.order, p.per_xcd, CAUSAL, qb, slice);
+    const int q0 = qb * kBlockM;
+    const int qi = q0 + wave * 32 + l32;   // this lane's query row
+
+    const uint16_t *Qs = static_cast<const uint16_t *>(p.Q) + (size_t)slice * p.S_q * p.D_qk;
+    const uint16_t *Ks = static_cast<const uint16_t *>(p.K) + (size_t)slice * p.S_k * p.D_qk;
+    const uint16_t *Vs = static_cast<const uint16_t *>(p.V) + (size_t)slice * p.S_k * p.D_v;
+
+    // Q fragment: B operand of S^T = K Q^T.  Lane (l32, hh) holds query qi,
+    // dims 16*st + 8*hh + 0..7 for step st.
+    u32x4 qf[DQ / 16];
+#pragma unroll
+    for (int st = 0; st < DQ / 16; ++st) {
+        const int d0 = st * 16 + hh * 8;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (qi < p.S_q) {
+            if (p.vec) {
+                if (d0 < p.D_qk)
+                    x = *reinterpret_cast<const u32x4 *>(Qs + (size_t)qi * p.D_qk + d0);
+            } else {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int d = d0 + 2 * e;
+                    const uint32_t lo = d < p.D_qk ? Qs[(size_t)qi * p.D_qk + d] : 0u;
+                    const uint32_t hi = d + 1 < p.D_qk ? Qs[(size_t)qi * p.D_qk + d + 1] : 0u;
+                    w[e] = lo | (hi << 16);
+                }
+                x = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+        x = (x ^ p.q_xor) & p.q_and;
+        // padded dims must stay exactly zero after the sign flip
+        if (d0 >= p.D_qk) x = u32x4{0u, 0u, 0u, 0u};
+        qf[st] = x;
+    }
+
+    const int ntiles = kv_tiles_for(qb, kBlockM, BN, p.S_q, p.S_k, CAUSAL);
+    const float c = p.c;
+
+    f32x16 o[DV / 32];
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
+    float m = neg_inf();   // running max of the raw scores of this query
+    float l = 0.0f;        // running sum of this lane's half of the keys
+
+    Regs16<DQ, DV> rg;
+    load_tile16<DQ, DV>(rg, Ks, Vs, 0, p, tid);
+    store_tile16<DQ, DV>(rg, lds, tid);
+    __syncthreads();
+
+    const int krow0 = sigma(l32);   // key row (within a 32-key block) for this lane
+    const int vrow0 = sigma(l32);   // V^T row (dim within a 32-dim block)
+
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load_tile16<DQ, DV>(rg, Ks, Vs, (t + 1) * BN, p, tid);
+
+        const u32x4 *Kl = lds + (t & 1) * T::STAGE;
+        const u32x4 *Vl = Kl + T::K_CHUNKS;
+        const int kbase = t * BN;
+
+        // ---- scores S^T (two 32-key blocks)
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{};
+            const int row = kb * 32 + krow0;
+#pragma unroll
+            for (int st = 0; st < DQ / 16; ++st) {
+                const u32x4 a = Kl[row * T::KCH + ((2 * st + hh) ^ swz(row))];
+                s[kb] = mma16<BF16>(a, qf[st], s[kb]);
+            }
+        }
+
+        // ---- masks: keys beyond S_k, and keys after the query when causal
+        const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > q0);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kbase + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
+                    bool ok = key < p.S_k;
+                    if (CAUSAL) ok = ok && key <= qi;
+                    s[kb][r] = ok ? s[kb][r] : neg_inf();
+                }
+        }
+
+        // ---- running max (in-lane over 32 keys, then with the other half)
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, other_half(mx));
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2((m - m_new) * c);
+        const float mc = m_new * c;
+        m = m_new;
+
+        // ---- P = exp(s - m), row sum, pack to 16-bit B operands
+        u32x4 pf[2][2];
+        float rs = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                uint32_t w[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * u + 2 * j], c, -mc));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * u + 2 * j + 1], c, -mc));
+                    rs += p0 + p1;
+                    w[j] = pack2<BF16>(p0, p1);
+                }
+                pf[kb][u] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        l = l * alpha + rs;
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int d = 0; d < DV / 32; ++d) {
+                    const int row = d * 32 + vrow0;
+                    const u32x4 a = Vl[row * T::VCH + ((kb * 4 + u * 2 + hh) ^ swz(row))];
+                    o[d] = mma16<BF16>(a, pf[kb][u], o[d]);
+                }
+
+        if (t + 1 < ntiles) store_tile16<DQ, DV>(rg, lds + ((t + 1) & 1) * T::STAGE, tid);
+        __syncthreads();
+    }
+
+    // ---- epilogue: O = O_acc / l, LSE = m*scale + ln(l)
+    const float lt = l + other_half(l);
+    const float inv = 1.0f / lt;
+    if (qi < p.S_q) {
+        uint16_t *Os = static_cast<uint16_t *>(p.O) + ((size_t)slice * p.S_q + qi) * p.D_v;
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int d0 = d * 32 + u * 16 + hh * 8;   // 8 consecutive dims
+                uint32_t w[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    w[j] = pack2<BF16>(o[d][8 * u + 2 * j] * inv, o[d][8 * u + 2 * j + 1] * inv);
+                if (p.vec) {
+                    if (d0 < p.D_v) *reinterpret_cast<u32x4 *>(Os + d0) = u32x4{w[0], w[1], w[2], w[3]};
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        if (d0 + j < p.D_v) Os[d0 + j] = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
+                }
+            }
+        if (p.LSE && hh == 0)
+            p.LSE[(size_t)slice * p.S_q + qi] = (m * c + __builtin_amdgcn_logf(lt)) * kLn2;
+    }
+}
+
+// ====================================================================
+// f32 kernel (v_mfma_f32_32x32x2_f32)
+// ====================================================================
+template <int DQ, int DV>
+struct Tile32 {
+    static constexpr int BN = 32;
+    static constexpr int KCH = DQ / 4;   // 16-byte chunks per K row
+    static constexpr int VCH = DV / 4;   // 16-byte chunks per V row
+    static constexpr int K_CHUNKS = BN * KCH;
+    static constexpr int V_CHUNKS = BN * VCH;
+    static constexpr int STAGE = K_CHUNKS + V_CHUNKS;
+    static constexpr int K_PER_T = K_CHUNKS / kThreads;
+    static constexpr int V_PER_T = V_CHUNKS / kThreads;
+    static_assert(K_CHUNKS % kThreads == 0 && V_CHUNKS % kThreads == 0, "tile split");
+};
+
+template <int DQ, int DV>
+struct Regs32 {
+    u32x4 k[Tile32<DQ, DV>::K_PER_T];
+    u32x4 v[Tile32<DQ, DV>::V_PER_T];
+};
+
+__device__ inline u32x4 load_f32x4(const float *__restrict__ base, int row, int nrows, int col,
+                                   int ncols, int vec)
+{
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (row < nrows) {
+        if (vec) {
+            if (col < ncols)
+                x = *reinterpret_cast<const u32x4 *>(base + (size_t)row * ncols + col);
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = col + e < ncols
+                           ? __builtin_bit_cast(uint32_t, base[(size_t)row * ncols + col + e])
+                           : 0u;
+            x = u32x4{w[0], w[1], w[2], w[3]};
+        }
+    }
+    return x;
+}
+
+template <int DQ, int DV>
+__device__ inline void load_tile32(Regs32<DQ, DV> &r, const float *__restrict__ Ks,
+                                   const float *__restrict__ Vs, int kbase, const KernelArgs &p,
+                                   int tid)
+{
+    using T = Tile32<DQ, DV>;
+#pragma unroll
+    for (int it = 0; it < T::K_PER_T; ++it) {
+        const int ci = tid + kThreads * it;
+        r.k[it] = load_f32x4(Ks, kbase + ci / T::KCH, p.S_k, (ci % T::KCH) * 4, p.D_qk, p.vec);
+    }
+#pragma unroll
+    for (int it = 0; it < T::V_PER_T; ++it) {
+        const int ci = tid + kThreads * it;
+        r.v[it] = load_f32x4(Vs, kbase + ci / T::VCH, p.S_k, (ci % T::VCH) * 4, p.D_v, p.vec);
+    }
+}
+
+template <int DQ, int DV>
+__device__ inline void store_tile32(const Regs32<DQ, DV> &r, u32x4 *__restrict__ stage, int tid)
+{
+    using T = Tile32<DQ, DV>;
+#pragma unroll
+    for (int it = 0; it < T::K_PER_T; ++it) {
+        const int ci = tid + kThreads * it;
+        const int row = ci / T::KCH, c = ci % T::KCH;
+        stage[row * T::KCH + (c ^ (row & 7))] = r.k[it];
+    }
+#pragma unroll
+    for (int it = 0; it < T::V_PER_T; ++it) {
+        const int ci = tid + kThreads * it;
+        stage[T::K_CHUNKS + ci] = r.v[it];
+    }
+}
+
+template <int DQ, int DV, bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+attn_fwd_32(KernelArgs p)
+{
+    using T = Tile32<DQ, DV>;
+    constexpr int BN = T::BN;
+    __shared__ u32x4 lds[2 * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, l32 = lane & 31;
+
+    int32_t qb, slice;
+    map_block((int32_t)blockIdx.x, p.q_blocks, p.slices, p.order, p.per_xcd, CAUSAL, qb, slice);
+    const int q0 = qb * kBlockM;
+    const int qi = q0 + wave * 32 + l32;
+
+    const float *Qs = static_cast<const float *>(p.Q) + (size_t)slice * p.S_q * p.D_qk;
+    const float *Ks = static_cast<const float *>(p.K) + (size_t)slice * p.S_k * p.D_qk;
+    const float *Vs = static_cast<const float *>(p.V) + (size_t)slice * p.S_k * p.D_v;
+
+    // Q fragment: step 4u+j of the k=2 MFMA uses dim 8u + 4hh + j.
+    float qf[DQ / 2];
+#pragma unroll
+    for (int u = 0; u < DQ / 8; ++u) {
+        u32x4 x = load_f32x4(Qs, qi, p.S_q, u * 8 + hh * 4, p.D_qk, p.vec);
+        x = (x ^ p.q_xor) & p.q_and;
+        // Bit-cast the whole vector: hipcc mis-compiles a bit_cast of a single
+        // ext-vector element (it reads element 0 for every index).
+        const f32x4 xf = __builtin_bit_cast(f32x4, x);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qf[4 * u + j] = (u * 8 + hh * 4 + j < p.D_qk) ? xf[j] : 0.0f;
+    }
+
+    const int ntiles = kv_tiles_for(qb, kBlockM, BN, p.S_q, p.S_k, CAUSAL);
+    const float c = p.c;
+
+    f32x16 o[DV / 32];
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
+    float m = neg_inf();
+    float l = 0.0f;
+
+    Regs32<DQ, DV> rg;
+    load_tile32<DQ, DV>(rg, Ks, Vs, 0, p, tid);
+    store_tile32<DQ, DV>(rg, lds, tid);
+    __syncthreads();
+
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) load_tile32<DQ, DV>(rg, Ks, Vs, (t + 1) * BN, p, tid);
+
+        const u32x4 *Kl = lds + (t & 1) * T::STAGE;
+        const float *Vl = reinterpret_cast<const float *>(Kl + T::K_CHUNKS);
+        const int kbase = t * BN;
+
+        // ---- S^T: lane (l32, hh) gets keys (r/4)*8 + 4hh + r%4 of query qi
+        f32x16 s = f32x16{};
+#pragma unroll
+        for (int u = 0; u < DQ / 8; ++u) {
+            const f32x4 a = __builtin_bit_cast(f32x4, Kl[l32 * T::KCH + ((2 * u + hh) ^ (l32 & 7))]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                s = mma32(a[j], qf[4 * u + j], s);
+        }
+
+        const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > q0);
+        if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kbase + (r >> 2) * 8 + hh * 4 + (r & 3);
+                bool ok = key < p.S_k;
+                if (CAUSAL) ok = ok && key <= qi;
+                s[r] = ok ? s[r] : neg_inf();
+            }
+        }
+
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, other_half(mx));
+        const float m_new = fmaxf(m, mx);
+        const float alpha = fast_exp2((m - m_new) * c);
+        const float mc = m_new * c;
+        m = m_new;
+
+        float pv[16];
+        float rs = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            pv[r] = fast_exp2(__builtin_fmaf(s[r], c, -mc));
+            rs += pv[r];
+        }
+        l = l * alpha + rs;
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+
+        // ---- O^T += V^T P^T; step r uses key (r/4)*8 + 4hh + r%4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int key = (r >> 2) * 8 + hh * 4 + (r & 3);
+#pragma unroll
+            for (int d = 0; d < DV / 32; ++d)
+                o[d] = mma32(Vl[key * DV + d * 32 + l32], pv[r], o[d]);
+        }
+
+        if (t + 1 < ntiles) store_tile32<DQ, DV>(rg, lds + ((t + 1) & 1) * T::STAGE, tid);
+        __syncthreads();
+    }
+
+    const float lt = l + other_half(l);
+    const float inv = 1.0f / lt;
+    if (qi < p.S_q) {
+        float *Os = static_cast<float *>(p.O) + ((size_t)slice * p.S_q + qi) * p.D_v;
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = d * 32 + g * 8 + hh * 4;   // 4 consecutive dims
+                f32x4 v4 = {o[d][4 * g] * inv, o[d][4 * g + 1] * inv, o[d][4 * g + 2] * inv,
+                            o[d][4 * g + 3] * inv};
+                if (p.vec) {
+                    if (d0 < p.D_v) *reinterpret_cast<f32x4 *>(Os + d0) = v4;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (d0 + j < p.D_v) Os[d0 + j] = v4[j];
+                }
+            }
+        if (p.LSE && hh == 0)
+            p.LSE[(size_t)slice * p.S_q + qi] = (m * c + __builtin_amdgcn_logf(lt)) * kLn2;
+    }
+}
+
+int pad_dim(int64_t d) { return d <= 64 ? 64 : 128; }
+
+template <typename Kern>
+hipError_t launch(Kern kern, int64_t grid, const KernelArgs &args, hipStream_t stream)
+{
+    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kThreads), 0, stream, args);
+    return hipGetLastError();
+}
+
+template <int DQ, int DV>
+hipError_t dispatch_causal(int dtype, bool causal, int64_t grid, const KernelArgs &a,
+                           hipStream_t s)
+{
+    if (dtype == TSD_F32)
+        return causal ? launch(attn_fwd_32<DQ, DV, true>, grid, a, s)
+                      : launch(attn_fwd_32<DQ, DV, false>, grid, a, s);
+    if (dtype == TSD_BF16)
+        return causal ? launch(attn_fwd_16<DQ, DV, true, true>, grid, a, s)
+                      : launch(attn_fwd_16<DQ, DV, false, true>, grid, a, s);
+    return causal ? launch(attn_fwd_16<DQ, DV, true, false>, grid, a, s)
+                  : launch(attn_fwd_16<DQ, DV, false, false>, grid, a, s);
+}
+
+}  // namespace
+
+TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v)
+{
+    TileConfig t;
+    t.block_m = kBlockM;
+    t.waves = kThreads / 64;
+    t.threads = kThreads;
+    t.dqk_block = pad_dim(D_qk);
+    t.dv_block = pad_dim(D_v);
+    if (dtype == TSD_F32) {
+        t.block_n = 32;
+        t.lds_bytes = 2 * (32 * t.dqk_block + 32 * t.dv_block) * 4;
+    } else {
+        t.block_n = 64;
+        t.lds_bytes = 2 * (64 * t.dqk_block + t.dv_block * 64) * 2;
+    }
+    return t;
+}
+
+hipError_t launch_attn(const TileConfig &cfg, int dtype, bool causal, int64_t grid,
+                       const KernelArgs &args, hipStream_t stream)
+{
+    if (cfg.dqk_block == 64 && cfg.dv_block == 64)
+        return dispatch_causal<64, 64>(dtype, causal, grid, args, stream);
+    if (cfg.dqk_block == 64 && cfg.dv_block == 128)
+        return dispatch_causal<64, 128>(dtype, causal, grid, args, stream);
+    if (cfg.dqk_block == 128 && cfg.dv_block == 64)
+        return dispatch_causal<128, 64>(dtype, causal, grid, args, stream);
+    return dispatch_causal<128, 128>(dtype, causal, grid, args, stream);
+}
+
+}  // namespace tsd

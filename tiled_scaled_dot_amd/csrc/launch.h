@@ -1,0 +1,82 @@
+// Internal interface between the host-side planner (attn_api.hip) and the
+// gfx950 kernels (attn_kernels.hip).  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tsd_attn.h"
+
+namespace tsd {
+
+// Kernel arguments (passed by value).  Pointers address slice 0; the kernel
+// adds the slice offset itself.
+struct KernelArgs {
+    const void *Q;
+    const void *K;
+    const void *V;
+    void *O;
+    float *LSE;        // may be null
+    int32_t S_q, S_k, D_qk, D_v;
+    int32_t q_blocks;  // per slice
+    int32_t slices;    // B * H
+    int32_t order;     // block order, see map_block
+    int32_t per_xcd;   // slices per XCD when order == 1
+    float c;           // |scale| * log2(e); 1 when scale == 0
+    uint32_t q_xor;    // XOR applied to every Q storage word (sign flip)
+    uint32_t q_and;    // AND applied to every Q storage word (0 zeroes Q)
+    int32_t vec;       // 1: 16-byte global accesses are legal
+};
+
+// Workgroup index -> (query block, slice).
+//
+// Query blocks are issued heaviest first when causal (the last query block
+// visits the most key tiles).  With order == 1 the slices are grouped so
+// that every workgroup of one slice lands on the same XCD: the dispatcher
+// hands consecutive workgroup ids to the 8 XCDs in turn, so id % 8 selects
+// the XCD and each XCD walks its own slices, keeping a slice's K/V tiles in
+// that XCD's L2.
+__host__ __device__ inline void map_block(int32_t block, int32_t q_blocks, int32_t slices,
+                                          int32_t order, int32_t per_xcd, bool heaviest_first,
+                                          int32_t &q_block, int32_t &slice)
+{
+    int32_t rank;
+    if (order == 1) {
+        const int32_t xcd = block & 7;
+        const int32_t j = block >> 3;
+        rank = j / per_xcd;
+        slice = (j - rank * per_xcd) * 8 + xcd;
+    } else {
+        rank = block / slices;
+        slice = block - rank * slices;
+    }
+    q_block = heaviest_first ? (q_blocks - 1 - rank) : rank;
+}
+
+// Key tiles visited by query block `q_block`: all tiles, or, when causal,
+// those holding a key <= the block's last valid query.
+__host__ __device__ inline int32_t kv_tiles_for(int32_t q_block, int32_t block_m, int32_t block_n,
+                                                int32_t S_q, int32_t S_k, bool causal)
+{
+    int32_t kv_len = S_k;
+    if (causal) {
+        int32_t q_last = (q_block + 1) * block_m;
+        if (q_last > S_q) q_last = S_q;
+        if (q_last < kv_len) kv_len = q_last;   // keys 0 .. q_last-1
+    }
+    return (kv_len + block_n - 1) / block_n;
+}
+
+// Fill the kernel's tile configuration for a dtype (shared by the planner
+// and the launcher so both agree).
+struct TileConfig {
+    int32_t block_m, block_n, waves, threads, dqk_block, dv_block, lds_bytes;
+};
+
+TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v);
+
+// Launch the kernel that matches (dtype, dqk_block, dv_block, causal).
+hipError_t launch_attn(const TileConfig &cfg, int dtype, bool causal, int64_t grid,
+                       const KernelArgs &args, hipStream_t stream);
+
+}  // namespace tsd
