@@ -145,16 +145,23 @@ def expected_tiles(qb, bm, bn, S_q, S_k, causal):
 def test_plan_for_workloads(lib, name):
     w = WORKLOADS[name]
     plan = tsd.attn_fwd_plan(w.B, w.H, w.S_q, w.S_k, w.D_qk, w.D_v, w.causal, w.dtype)
-    assert plan.block_m == 128 and plan.threads == 256 and plan.waves == 4
-    assert plan.block_n == (32 if w.dtype == "f32" else 64)
+    if w.dtype == "f32":
+        # generic kernel: 4 waves x 32 rows, 32-key tiles, two LDS stages
+        assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (128, 256, 4, 32)
+        assert plan.lds_bytes <= 64 * 1024
+    else:
+        # LDS-direct kernel: 8 waves x 32 rows, 64-key tiles, three LDS stages
+        assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (256, 512, 8, 64)
+        assert plan.lds_bytes == 3 * 64 * (plan.dqk_block + plan.dv_block) * 2
+        assert plan.lds_bytes <= 160 * 1024
+    bm = plan.block_m
     assert plan.dqk_block >= w.D_qk and plan.dv_block >= w.D_v
-    assert plan.lds_bytes <= 64 * 1024
     assert plan.slices == w.B * w.H
-    assert plan.q_blocks == math.ceil(w.S_q / 128)
+    assert plan.q_blocks == math.ceil(w.S_q / bm)
     assert plan.kv_blocks == math.ceil(w.S_k / plan.block_n)
     assert plan.grid == plan.q_blocks * plan.slices
     assert plan.order == (1 if plan.slices % 8 == 0 else 0)
-    total = sum(expected_tiles(qb, 128, plan.block_n, w.S_q, w.S_k, w.causal)
+    total = sum(expected_tiles(qb, bm, plan.block_n, w.S_q, w.S_k, w.causal)
                 for qb in range(plan.q_blocks)) * plan.slices
     assert plan.total_kv_steps == total
 
@@ -171,7 +178,7 @@ def test_block_map_covers_each_tile_once(lib, B, H, S_q, S_k, causal):
     for blk in range(plan.grid):
         qb, sl, steps = tsd.attn_fwd_plan_block(plan, S_q, S_k, blk)
         assert 0 <= qb < plan.q_blocks and 0 <= sl < plan.slices
-        assert steps == expected_tiles(qb, 128, plan.block_n, S_q, S_k, causal)
+        assert steps == expected_tiles(qb, plan.block_m, plan.block_n, S_q, S_k, causal)
         seen.add((qb, sl))
         steps_in_order.append(steps)
         if plan.order == 1:

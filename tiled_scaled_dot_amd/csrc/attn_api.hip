@@ -56,7 +56,7 @@ int check_shape(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, in
 void fill_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
                int causal, int dtype, bool vector_io, tsd_plan *pl)
 {
-    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v);
+    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, vector_io);
     std::memset(pl, 0, sizeof(*pl));
     pl->dtype = dtype;
     pl->causal = causal ? 1 : 0;
@@ -176,7 +176,7 @@ extern "C" int attn_fwd(const void *Q, const void *K, const void *V, void *O, fl
     a.q_and = scale == 0.0f ? 0u : 0xffffffffu;
     a.vec = vec ? 1 : 0;
 
-    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v);
+    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, vec);
     hipError_t err = tsd::launch_attn(cfg, dtype, causal != 0, plan.grid, a,
                                       reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? TSD_OK : TSD_ERR_HIP;

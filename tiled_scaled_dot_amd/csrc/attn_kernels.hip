@@ -609,13 +609,336 @@ attn_fwd_32(KernelArgs p)
     }
 }
 
+// ====================================================================
+// Fast 16-bit kernel (vector-aligned inputs, D_qk and D_v multiples of 8).
+//
+//   * 8 waves x 32 query rows = 256 rows per workgroup, one workgroup per
+//     CU (2 waves per SIMD), so one LDS copy of each K/V tile feeds 8 waves.
+//   * K and V tiles (64 keys) go HBM -> LDS directly with buffer loads
+//     (buffer_load_dwordx4 ... lds): no VGPR staging, no LDS write
+//     instructions.  The buffer range is the slice, so key rows >= S_k read
+//     as zero; head-dim chunks >= D read as zero through an out-of-range
+//     offset.  Three LDS stages keep two tiles in flight.
+//   * Each wave instruction fills 1 KB of LDS contiguously (lane i -> bytes
+//     16i..16i+15); the swizzle is realised by choosing which global chunk
+//     each lane fetches.
+//   * V stays row-major in LDS; the A operand of O^T += V^T P^T is read with
+//     ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives
+//     element i%4 of the 8-byte chunks addressed by lanes i/4, 4+i/4, 8+i/4
+//     and 12+i/4, so lanes pointing at 4 consecutive key rows hand every lane
+//     4 keys of one head-dim column.
+//   * The running max is only moved when some row's max grows by more than
+//     2^kTau (wave-uniform decision); in between, P = 2^(s*c - m*c) may reach
+//     2^kTau.  O/l is unchanged in real arithmetic, and the rescale of O and
+//     l becomes rare.
+//   * O and LSE are written with buffer stores; stores outside the slice are
+//     dropped by the hardware range check.
+// ====================================================================
+constexpr int kFastWaves = 8;
+constexpr int kFastThreads = kFastWaves * 64;
+constexpr int kFastBlockM = kFastWaves * 32;
+constexpr float kTau = 8.0f;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // above any slice size (< 2^31 bytes)
+constexpr int kBufferConfig = 0x00020000;       // raw buffer, 32-bit data format
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+template <int DQ, int DV>
+struct Fast16 {
+    static constexpr int BN = 64;
+    static constexpr int ST = 3;                       // LDS stages
+    static constexpr int KROW = DQ * 2, VROW = DV * 2; // bytes per row in LDS
+    static constexpr int KCH = DQ / 8, VCH = DV / 8;   // 16-byte chunks per row
+    static constexpr int KT = BN * KROW, VT = BN * VROW;
+    static constexpr int STAGE = KT + VT;
+    static constexpr int K_PER_W = KT / 1024 / kFastWaves;   // 1 KB load instructions per wave
+    static constexpr int V_PER_W = VT / 1024 / kFastWaves;
+    static constexpr int LOADS = K_PER_W + V_PER_W;          // per wave per tile
+    static_assert(K_PER_W >= 1 && V_PER_W >= 1, "tile split");
+};
+
+// V chunk swizzle: 16-byte chunk c of key row r is stored at c ^ (2*(r%4)),
+// so the 4 consecutive rows x 32 bytes of one transposed read hit 8
+// different 16-byte bank groups.
+__device__ inline int vswz(int row) { return (row & 3) << 1; }
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kBufferConfig);
+}
+
+// The same raw buffer descriptor as four scalar words, for inline asm.
+__device__ inline u32x4 rsrc_words(const void *base, uint32_t bytes)
+{
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kBufferConfig};
+}
+
+// One wave instruction: 64 lanes x 16 bytes from the buffer (lane offset
+// `voffset`, zero when out of range) into LDS bytes lds_addr + 16*lane.
+// Issued through inline asm on purpose: the compiler's wait-count pass
+// treats a transposed LDS read as aliasing every pending LDS-DMA load and
+// would wait for the whole prefetch pipeline before it; the kernel keeps the
+// vmcnt bookkeeping itself (wait_loads) and VMEM loads complete in order.
+__device__ inline void dma16(uint32_t lds_addr, uint32_t voffset, u32x4 rsrc)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(voffset), "s"(rsrc)
+                 : "memory", "m0");
+}
+
+__device__ inline uint32_t lds_address(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)(p);
+}
+
+template <int LOADS_LEFT>
+__device__ inline void wait_loads()
+{
+    // s_waitcnt vmcnt(LOADS_LEFT), expcnt / lgkmcnt left at their maximum.
+    static_assert(LOADS_LEFT >= 0 && LOADS_LEFT < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((LOADS_LEFT & 15) | ((LOADS_LEFT >> 4) << 14) | (7 << 4) |
+                               (15 << 8));
+}
+
+template <int DQ, int DV, bool CAUSAL, bool BF16>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kFastThreads, kFastThreads),
+                               amdgpu_waves_per_eu(2, 2)))
+attn_fwd_fast16(KernelArgs p)
+{
+    using T = Fast16<DQ, DV>;
+    constexpr int BN = T::BN;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::ST * T::STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hh = lane >> 5, l32 = lane & 31;
+
+    int32_t qb, slice;
+    map_block((int32_t)blockIdx.x, p.q_blocks, p.slices, p.order, p.per_xcd, CAUSAL, qb, slice);
+    const int q0 = qb * kFastBlockM;
+    const int qw = q0 + wave * 32;          // first query row of this wave
+    const int qi = qw + l32;                // this lane's query row
+
+    const uint32_t q_bytes = (uint32_t)p.S_q * p.D_qk * 2;
+    const uint32_t k_bytes = (uint32_t)p.S_k * p.D_qk * 2;
+    const uint32_t v_bytes = (uint32_t)p.S_k * p.D_v * 2;
+    const uint32_t o_bytes = (uint32_t)p.S_q * p.D_v * 2;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(static_cast<const uint8_t *>(p.Q) + (size_t)slice * q_bytes, q_bytes);
+    const u32x4 rk = rsrc_words(static_cast<const uint8_t *>(p.K) + (size_t)slice * k_bytes, k_bytes);
+    const u32x4 rv = rsrc_words(static_cast<const uint8_t *>(p.V) + (size_t)slice * v_bytes, v_bytes);
+
+    // ---- per-lane source offsets of this wave's K/V load instructions
+    uint32_t koff[T::K_PER_W], voff[T::V_PER_W];
+#pragma unroll
+    for (int j = 0; j < T::K_PER_W; ++j) {
+        const int P = (wave * T::K_PER_W + j) * 64 + lane;   // chunk slot in the K tile
+        const int row = P / T::KCH, c = (P % T::KCH) ^ swz(row);
+        koff[j] = c * 8 < p.D_qk ? (uint32_t)(row * p.D_qk + c * 8) * 2 : kOutOfRange;
+    }
+#pragma unroll
+    for (int j = 0; j < T::V_PER_W; ++j) {
+        const int P = (wave * T::V_PER_W + j) * 64 + lane;
+        const int row = P / T::VCH, c = (P % T::VCH) ^ vswz(row);
+        voff[j] = c * 8 < p.D_v ? (uint32_t)(row * p.D_v + c * 8) * 2 : kOutOfRange;
+    }
+    const uint32_t lds_k0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+        lds_address(smem) + (uint32_t)wave * T::K_PER_W * 1024);
+    const uint32_t lds_v0 = (uint32_t)__builtin_amdgcn_readfirstlane(
+        lds_address(smem) + T::KT + (uint32_t)wave * T::V_PER_W * 1024);
+    auto issue_tile = [&](int t) {
+        const uint32_t st = (uint32_t)(t % T::ST) * T::STAGE;
+        const uint32_t kb = (uint32_t)t * BN * p.D_qk * 2;
+        const uint32_t vb = (uint32_t)t * BN * p.D_v * 2;
+#pragma unroll
+        for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + st + j * 1024, koff[j] + kb, rk);
+#pragma unroll
+        for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + st + j * 1024, voff[j] + vb, rv);
+    };
+
+    const int ntiles = kv_tiles_for(qb, kFastBlockM, BN, p.S_q, p.S_k, CAUSAL);
+#pragma unroll
+    for (int t = 0; t < T::ST - 1; ++t)
+        if (t < ntiles) issue_tile(t);
+
+    // ---- Q fragment (B operand of S^T = K Q^T): query qi, dims 16st + 8hh + 0..7
+    u32x4 qf[DQ / 16];
+#pragma unroll
+    for (int st = 0; st < DQ / 16; ++st) {
+        const int d0 = st * 16 + hh * 8;
+        const uint32_t off = d0 < p.D_qk ? (uint32_t)(qi * p.D_qk + d0) * 2 : kOutOfRange;
+        u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+        x = (x ^ p.q_xor) & p.q_and;
+        if (d0 >= p.D_qk) x = u32x4{0u, 0u, 0u, 0u};
+        qf[st] = x;
+    }
+
+    // ---- per-lane LDS read offsets
+    // K (score A operand): row 32kb + sigma(l32), chunk (2st + hh) ^ swz(row).
+    const int krow = sigma(l32);
+    const int kswz = swz(krow);
+    // V (transposed reads): group g = lane/16, i = lane%16, source lane
+    // i = 4k + q points at key row (... + k), dims 32*dblk + 16*(g%2) + 4q.
+    const int vg = lane >> 4, vi = lane & 15, vk = vi >> 2, vq = vi & 3;
+    const int vchunk_lo = (vg & 1) * 2 + (vq >> 1);   // chunk within the 4-chunk dblk group
+
+    f32x16 o[DV / 32];
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
+    const float c = p.c;
+    float m = neg_inf();
+    float l = 0.0f;
+
+    for (int t = 0; t < ntiles; ++t) {
+        if (t + 1 < ntiles) wait_loads<T::LOADS>();
+        else wait_loads<0>();
+        __syncthreads();
+        if (t + T::ST - 1 < ntiles) issue_tile(t + T::ST - 1);
+
+        const int kbase = t * BN;
+        if (CAUSAL && kbase > qw + 31) continue;   // every key of this tile is after every row
+
+        const uint8_t *Kl = smem + (t % T::ST) * T::STAGE;
+        const uint8_t *Vl = Kl + T::KT;
+
+        // ---- scores S^T (two 32-key blocks)
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{};
+            const uint8_t *kr = Kl + (kb * 32 + krow) * T::KROW;
+#pragma unroll
+            for (int st = 0; st < DQ / 16; ++st) {
+                const u32x4 a = *reinterpret_cast<const u32x4 *>(kr + ((2 * st + hh) ^ kswz) * 16);
+                s[kb] = mma16<BF16>(a, qf[st], s[kb]);
+            }
+        }
+
+        // ---- masks: keys >= S_k; keys after the query when causal
+        const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > qw);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kbase + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
+                    bool ok = key < p.S_k;
+                    if (CAUSAL) ok = ok && key <= qi;
+                    s[kb][r] = ok ? s[kb][r] : neg_inf();
+                }
+        }
+
+        // ---- running max; rescale only when a row's max grows by > 2^kTau
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, other_half(mx));
+        const bool grow = (mx - m) * c > kTau;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = fast_exp2((m - m_new) * c);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+        }
+        const float mc = m * c;
+
+        // ---- P = 2^(s c - m c) packed to 16 bits; the row sum is taken over
+        // the f32 values so that LSE keeps f32 accuracy
+        u32x4 pf[2][2];
+        float rs0 = 0.0f, rs1 = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                uint32_t w[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * u + 2 * j], c, -mc));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * u + 2 * j + 1], c, -mc));
+                    rs0 += p0;
+                    rs1 += p1;
+                    w[j] = pack2<BF16>(p0, p1);
+                }
+                pf[kb][u] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        l += rs0 + rs1;
+
+        // ---- O^T += V^T P^T; the A operand comes from two transposed reads
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+#pragma unroll
+                for (int d = 0; d < DV / 32; ++d) {
+                    uint32_t a[4];
+#pragma unroll
+                    for (int sh = 0; sh < 2; ++sh) {
+                        const int row = kb * 32 + u * 16 + hh * 8 + sh * 4 + vk;
+                        const int chunk = (d * 4 + vchunk_lo) ^ vswz(row);
+                        const uint8_t *src = Vl + row * T::VROW + chunk * 16 + (vq & 1) * 8;
+                        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4 *)(src));
+                        const u32x2 xw = __builtin_bit_cast(u32x2, x);
+                        a[2 * sh] = xw.x;
+                        a[2 * sh + 1] = xw.y;
+                    }
+                    o[d] = mma16<BF16>(u32x4{a[0], a[1], a[2], a[3]}, pf[kb][u], o[d]);
+                }
+            }
+    }
+
+    // ---- epilogue: O = O_acc / l, LSE = m*scale + ln(l)
+    const float lt = l + other_half(l);
+    const float inv = 1.0f / lt;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(static_cast<uint8_t *>(p.O) + (size_t)slice * o_bytes, o_bytes);
+    const bool row_ok = qi < p.S_q;
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+            const int d0 = d * 32 + g4 * 8 + hh * 4;   // 4 consecutive dims
+            const uint32_t w0 = pack2<BF16>(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv);
+            const uint32_t w1 = pack2<BF16>(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv);
+            const uint32_t off =
+                (row_ok && d0 < p.D_v) ? (uint32_t)(qi * p.D_v + d0) * 2 : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, u32x2{w0, w1}), ro,
+                                                  off, 0, 0);
+        }
+    if (p.LSE && hh == 0 && row_ok)
+        p.LSE[(size_t)slice * p.S_q + qi] = (m * c + __builtin_amdgcn_logf(lt)) * kLn2;
+}
+
 int pad_dim(int64_t d) { return d <= 64 ? 64 : 128; }
 
 template <typename Kern>
-hipError_t launch(Kern kern, int64_t grid, const KernelArgs &args, hipStream_t stream)
+hipError_t launch(Kern kern, int64_t grid, const KernelArgs &args, hipStream_t stream,
+                  int threads = kThreads)
 {
-    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(threads), 0, stream, args);
     return hipGetLastError();
+}
+
+template <int DQ, int DV>
+hipError_t dispatch_fast(int dtype, bool causal, int64_t grid, const KernelArgs &a,
+                         hipStream_t s)
+{
+    if (dtype == TSD_BF16)
+        return causal ? launch(attn_fwd_fast16<DQ, DV, true, true>, grid, a, s, kFastThreads)
+                      : launch(attn_fwd_fast16<DQ, DV, false, true>, grid, a, s, kFastThreads);
+    return causal ? launch(attn_fwd_fast16<DQ, DV, true, false>, grid, a, s, kFastThreads)
+                  : launch(attn_fwd_fast16<DQ, DV, false, false>, grid, a, s, kFastThreads);
 }
 
 template <int DQ, int DV>
@@ -634,18 +957,29 @@ hipError_t dispatch_causal(int dtype, bool causal, int64_t grid, const KernelArg
 
 }  // namespace
 
-TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v)
+TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec)
 {
     TileConfig t;
-    t.block_m = kBlockM;
-    t.waves = kThreads / 64;
-    t.threads = kThreads;
     t.dqk_block = pad_dim(D_qk);
     t.dv_block = pad_dim(D_v);
-    if (dtype == TSD_F32) {
+    t.fast = dtype != TSD_F32 && vec;
+    if (t.fast) {
+        using F = Fast16<128, 128>;
+        t.block_m = kFastBlockM;
+        t.waves = kFastWaves;
+        t.threads = kFastThreads;
+        t.block_n = F::BN;
+        t.lds_bytes = F::ST * F::BN * (t.dqk_block + t.dv_block) * 2;
+    } else if (dtype == TSD_F32) {
+        t.block_m = kBlockM;
+        t.waves = kThreads / 64;
+        t.threads = kThreads;
         t.block_n = 32;
         t.lds_bytes = 2 * (32 * t.dqk_block + 32 * t.dv_block) * 4;
     } else {
+        t.block_m = kBlockM;
+        t.waves = kThreads / 64;
+        t.threads = kThreads;
         t.block_n = 64;
         t.lds_bytes = 2 * (64 * t.dqk_block + t.dv_block * 64) * 2;
     }
@@ -655,13 +989,21 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v)
 hipError_t launch_attn(const TileConfig &cfg, int dtype, bool causal, int64_t grid,
                        const KernelArgs &args, hipStream_t stream)
 {
-    if (cfg.dqk_block == 64 && cfg.dv_block == 64)
-        return dispatch_causal<64, 64>(dtype, causal, grid, args, stream);
-    if (cfg.dqk_block == 64 && cfg.dv_block == 128)
-        return dispatch_causal<64, 128>(dtype, causal, grid, args, stream);
-    if (cfg.dqk_block == 128 && cfg.dv_block == 64)
-        return dispatch_causal<128, 64>(dtype, causal, grid, args, stream);
-    return dispatch_causal<128, 128>(dtype, causal, grid, args, stream);
+    const int key = (cfg.dqk_block == 128 ? 2 : 0) + (cfg.dv_block == 128 ? 1 : 0);
+    if (cfg.fast) {
+        switch (key) {
+        case 0: return dispatch_fast<64, 64>(dtype, causal, grid, args, stream);
+        case 1: return dispatch_fast<64, 128>(dtype, causal, grid, args, stream);
+        case 2: return dispatch_fast<128, 64>(dtype, causal, grid, args, stream);
+        default: return dispatch_fast<128, 128>(dtype, causal, grid, args, stream);
+        }
+    }
+    switch (key) {
+    case 0: return dispatch_causal<64, 64>(dtype, causal, grid, args, stream);
+    case 1: return dispatch_causal<64, 128>(dtype, causal, grid, args, stream);
+    case 2: return dispatch_causal<128, 64>(dtype, causal, grid, args, stream);
+    default: return dispatch_causal<128, 128>(dtype, causal, grid, args, stream);
+    }
 }
 
 }  // namespace tsd
