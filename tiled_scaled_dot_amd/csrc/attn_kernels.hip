@@ -56,6 +56,32 @@ __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Swap-half reduction partner: lane l <-> lane l ^ 32.
 __device__ inline float other_half(float x) { return __shfl_xor(x, 32); }
 
+// Cross-half reductions with one v_permlane32_swap (gfx950).  The
+// instruction exchanges the upper 32 lanes of its first operand with the
+// lower 32 lanes of its second; with both operands = x, every lane l ends up
+// holding {x[l], x[l^32]} across the two results (in an order that depends
+// on the half), so max / sum of the pair is the reduction over lanes l and
+// l^32 on every lane, bitwise identical within the pair.
+__device__ inline void swap32(float x, float &a, float &b)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __builtin_bit_cast(float, (uint32_t)r[0]);
+    b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ inline float max_halves(float x)
+{
+    float a, b;
+    swap32(x, a, b);
+    return fmaxf(a, b);
+}
+__device__ inline float sum_halves(float x)
+{
+    float a, b;
+    swap32(x, a, b);
+    return a + b;
+}
+
 // ---------------------------------------------------------------- MFMA
 template <bool BF16>
 __device__ inline f32x16 mma16(u32x4 a, u32x4 b, f32x16 c)
@@ -658,10 +684,20 @@ struct Fast16 {
     static_assert(K_PER_W >= 1 && V_PER_W >= 1, "tile split");
 };
 
-// V chunk swizzle: 16-byte chunk c of key row r is stored at c ^ (2*(r%4)),
-// so the 4 consecutive rows x 32 bytes of one transposed read hit 8
-// different 16-byte bank groups.
-__device__ inline int vswz(int row) { return (row & 3) << 1; }
+// LDS swizzles for the fast kernel.  gfx950's LDS has 64 banks of 4 bytes
+// (256 bytes per clock): a ds_read_b128 is serviced 16 lanes at a time and a
+// ds_read_b64_tr_b16 32 lanes at a time, and each such group must touch all
+// 64 banks to avoid conflicts.  16-byte chunk c of row r is stored at chunk
+// c ^ f(r):
+//   K (score A operand, 16 lanes read rows 0..15 of a block at one chunk):
+//     f(r) = r % 16 for 256-byte rows, (r / 2) % 8 for 128-byte rows;
+//   V (transposed reads, 32 lanes read 64 bytes from each of 4 consecutive
+//     rows): f(r) = 4 * (r % 4) for 256-byte rows, 4 * ((r / 2) % 2) for
+//     128-byte rows.
+template <int CHUNKS>
+__device__ inline int kswz(int row) { return CHUNKS == 16 ? (row & 15) : ((row >> 1) & 7); }
+template <int CHUNKS>
+__device__ inline int vswz(int row) { return CHUNKS == 16 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes)
 {
@@ -696,6 +732,9 @@ __device__ inline uint32_t lds_address(const void *p)
 {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t *)(p);
 }
+
+typedef const __attribute__((address_space(3))) uint8_t lds_u8;
+__device__ inline lds_u8 *lds_ptr(uint32_t addr) { return (lds_u8 *)(uintptr_t)addr; }
 
 template <int LOADS_LEFT>
 __device__ inline void wait_loads()
@@ -740,13 +779,13 @@ attn_fwd_fast16(KernelArgs p)
 #pragma unroll
     for (int j = 0; j < T::K_PER_W; ++j) {
         const int P = (wave * T::K_PER_W + j) * 64 + lane;   // chunk slot in the K tile
-        const int row = P / T::KCH, c = (P % T::KCH) ^ swz(row);
+        const int row = P / T::KCH, c = (P % T::KCH) ^ kswz<T::KCH>(row);
         koff[j] = c * 8 < p.D_qk ? (uint32_t)(row * p.D_qk + c * 8) * 2 : kOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < T::V_PER_W; ++j) {
         const int P = (wave * T::V_PER_W + j) * 64 + lane;
-        const int row = P / T::VCH, c = (P % T::VCH) ^ vswz(row);
+        const int row = P / T::VCH, c = (P % T::VCH) ^ vswz<T::VCH>(row);
         voff[j] = c * 8 < p.D_v ? (uint32_t)(row * p.D_v + c * 8) * 2 : kOutOfRange;
     }
     const uint32_t lds_k0 = (uint32_t)__builtin_amdgcn_readfirstlane(
@@ -780,14 +819,32 @@ attn_fwd_fast16(KernelArgs p)
         qf[st] = x;
     }
 
-    // ---- per-lane LDS read offsets
-    // K (score A operand): row 32kb + sigma(l32), chunk (2st + hh) ^ swz(row).
-    const int krow = sigma(l32);
-    const int kswz = swz(krow);
+    // ---- per-lane LDS read offsets (relative to a stage), computed once
+    // K (score A operand): row 32kb + sigma(l32), logical chunk 2st + hh.
+    // The swizzle depends on the row only through bits the kb term does not
+    // touch, so the kb offset is a constant added per read.
+    uint32_t kro[DQ / 16];
+    {
+        const int krow = sigma(l32);
+#pragma unroll
+        for (int st = 0; st < DQ / 16; ++st)
+            kro[st] = lds_address(smem) +
+                      (uint32_t)(krow * T::KROW + ((2 * st + hh) ^ kswz<T::KCH>(krow)) * 16);
+    }
     // V (transposed reads): group g = lane/16, i = lane%16, source lane
-    // i = 4k + q points at key row (... + k), dims 32*dblk + 16*(g%2) + 4q.
-    const int vg = lane >> 4, vi = lane & 15, vk = vi >> 2, vq = vi & 3;
-    const int vchunk_lo = (vg & 1) * 2 + (vq >> 1);   // chunk within the 4-chunk dblk group
+    // i = 4k + q points at key row R + k (R a multiple of 4: the swizzle only
+    // sees k and the row's low bits), dims 32*dblk + 16*(g%2) + 4q.
+    uint32_t vro[DV / 32];
+    {
+        const int vg = lane >> 4, vi = lane & 15, vk = vi >> 2, vq = vi & 3;
+        const int row = hh * 8 + vk;   // + 32kb + 16u + 4sh, multiples of 8 and 4
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d) {
+            const int chunk = (d * 4 + (vg & 1) * 2 + (vq >> 1)) ^ vswz<T::VCH>(row);
+            vro[d] = lds_address(smem) +
+                     (uint32_t)(T::KT + row * T::VROW + chunk * 16 + (vq & 1) * 8);
+        }
+    }
 
     f32x16 o[DV / 32];
 #pragma unroll
@@ -796,27 +853,35 @@ attn_fwd_fast16(KernelArgs p)
     float m = neg_inf();
     float l = 0.0f;
 
+    uint32_t stage_off = 0;   // byte offset of tile t's stage, rotating over ST stages
     for (int t = 0; t < ntiles; ++t) {
         if (t + 1 < ntiles) wait_loads<T::LOADS>();
         else wait_loads<0>();
         __syncthreads();
         if (t + T::ST - 1 < ntiles) issue_tile(t + T::ST - 1);
 
+        const uint32_t so = stage_off;
+        stage_off = (stage_off == (T::ST - 1) * T::STAGE) ? 0u : stage_off + T::STAGE;
         const int kbase = t * BN;
         if (CAUSAL && kbase > qw + 31) continue;   // every key of this tile is after every row
 
-        const uint8_t *Kl = smem + (t % T::ST) * T::STAGE;
-        const uint8_t *Vl = Kl + T::KT;
+        // per-tile read bases; the rest of each address is an immediate offset
+        uint32_t kaddr[DQ / 16], vaddr[DV / 32];
+#pragma unroll
+        for (int st = 0; st < DQ / 16; ++st) kaddr[st] = kro[st] + so;
+#pragma unroll
+        for (int d = 0; d < DV / 32; ++d) vaddr[d] = vro[d] + so;
 
         // ---- scores S^T (two 32-key blocks)
         f32x16 s[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             s[kb] = f32x16{};
-            const uint8_t *kr = Kl + (kb * 32 + krow) * T::KROW;
 #pragma unroll
             for (int st = 0; st < DQ / 16; ++st) {
-                const u32x4 a = *reinterpret_cast<const u32x4 *>(kr + ((2 * st + hh) ^ kswz) * 16);
+                const u32x4 a =
+                    *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                        lds_ptr(kaddr[st]) + kb * 32 * T::KROW);
                 s[kb] = mma16<BF16>(a, qf[st], s[kb]);
             }
         }
@@ -841,7 +906,7 @@ attn_fwd_fast16(KernelArgs p)
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, other_half(mx));
+        mx = max_halves(mx);
         const bool grow = (mx - m) * c > kTau;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             const float m_new = fmaxf(m, mx);
@@ -884,11 +949,8 @@ attn_fwd_fast16(KernelArgs p)
                     uint32_t a[4];
 #pragma unroll
                     for (int sh = 0; sh < 2; ++sh) {
-                        const int row = kb * 32 + u * 16 + hh * 8 + sh * 4 + vk;
-                        const int chunk = (d * 4 + vchunk_lo) ^ vswz(row);
-                        const uint8_t *src = Vl + row * T::VROW + chunk * 16 + (vq & 1) * 8;
                         const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4 *)(src));
+                            (lds_s16x4 *)(lds_ptr(vaddr[d]) + (kb * 32 + u * 16 + sh * 4) * T::VROW));
                         const u32x2 xw = __builtin_bit_cast(u32x2, x);
                         a[2 * sh] = xw.x;
                         a[2 * sh + 1] = xw.y;
@@ -899,7 +961,7 @@ attn_fwd_fast16(KernelArgs p)
     }
 
     // ---- epilogue: O = O_acc / l, LSE = m*scale + ln(l)
-    const float lt = l + other_half(l);
+    const float lt = sum_halves(l);
     const float inv = 1.0f / lt;
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(static_cast<uint8_t *>(p.O) + (size_t)slice * o_bytes, o_bytes);
