@@ -150,9 +150,10 @@ def test_plan_for_workloads(lib, name):
         assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (128, 256, 4, 32)
         assert plan.lds_bytes <= 64 * 1024
     else:
-        # LDS-direct kernel: 8 waves x 32 rows, 64-key tiles, three LDS stages
+        # LDS-direct kernel: 8 waves x 32 rows, 64-key tiles, K ring of 4 slots
+        # and V ring of 3 slots
         assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (256, 512, 8, 64)
-        assert plan.lds_bytes == 3 * 64 * (plan.dqk_block + plan.dv_block) * 2
+        assert plan.lds_bytes == (4 * plan.dqk_block + 3 * plan.dv_block) * 64 * 2
         assert plan.lds_bytes <= 160 * 1024
     bm = plan.block_m
     assert plan.dqk_block >= w.D_qk and plan.dv_block >= w.D_v

@@ -638,13 +638,16 @@ attn_fwd_32(KernelArgs p)
 // ====================================================================
 // Fast 16-bit kernel (vector-aligned inputs, D_qk and D_v multiples of 8).
 //
-//   * 8 waves x 32 query rows = 256 rows per workgroup, one workgroup per
-//     CU (2 waves per SIMD), so one LDS copy of each K/V tile feeds 8 waves.
+//   * 4 waves x 32 query rows = 128 rows per workgroup, two workgroups per
+//     CU (2 waves per SIMD from different workgroups, so their barriers do
+//     not lock the two waves of a SIMD into the same phase).
 //   * K and V tiles (64 keys) go HBM -> LDS directly with buffer loads
 //     (buffer_load_dwordx4 ... lds): no VGPR staging, no LDS write
 //     instructions.  The buffer range is the slice, so key rows >= S_k read
 //     as zero; head-dim chunks >= D read as zero through an out-of-range
-//     offset.  Three LDS stages keep two tiles in flight.
+//     offset.  K and V have two LDS slots each (64 KB at D = 128): a tile's
+//     K is read one iteration before its V, so K is fetched two tiles ahead
+//     and V one tile ahead.
 //   * Each wave instruction fills 1 KB of LDS contiguously (lane i -> bytes
 //     16i..16i+15); the swizzle is realised by choosing which global chunk
 //     each lane fetches.
@@ -660,9 +663,17 @@ attn_fwd_32(KernelArgs p)
 //   * O and LSE are written with buffer stores; stores outside the slice are
 //     dropped by the hardware range check.
 // ====================================================================
-constexpr int kFastWaves = 8;
+#ifndef TSD_FAST_WAVES
+#define TSD_FAST_WAVES 8
+#endif
+#ifndef TSD_FAST_VSLOTS
+#define TSD_FAST_VSLOTS 3
+#endif
+constexpr int kFastWaves = TSD_FAST_WAVES;   // waves per workgroup (4 or 8)
 constexpr int kFastThreads = kFastWaves * 64;
 constexpr int kFastBlockM = kFastWaves * 32;
+constexpr int kVSlots = TSD_FAST_VSLOTS;     // V ring size; the K ring has one slot more
+static_assert(kVSlots >= 2 && kVSlots <= 4, "V ring size");
 constexpr float kTau = 8.0f;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // above any slice size (< 2^31 bytes)
 constexpr int kBufferConfig = 0x00020000;       // raw buffer, 32-bit data format
@@ -673,14 +684,17 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 template <int DQ, int DV>
 struct Fast16 {
     static constexpr int BN = 64;
-    static constexpr int ST = 3;                       // LDS stages
     static constexpr int KROW = DQ * 2, VROW = DV * 2; // bytes per row in LDS
     static constexpr int KCH = DQ / 8, VCH = DV / 8;   // 16-byte chunks per row
     static constexpr int KT = BN * KROW, VT = BN * VROW;
-    static constexpr int STAGE = KT + VT;
+    // Ring buffers: VS slots for V and VS+1 for K.  K of tile t+1 is read in
+    // the same iteration as V of tile t, so K runs one tile ahead of V.
+    static constexpr int VS = kVSlots, KS = kVSlots + 1;
+    static constexpr int K_SLOT0 = 0, V_SLOT0 = KS * KT;
+    static constexpr int LDS_BYTES = KS * KT + VS * VT;
+    static constexpr int LOADS = KT / 1024 / kFastWaves + VT / 1024 / kFastWaves;
     static constexpr int K_PER_W = KT / 1024 / kFastWaves;   // 1 KB load instructions per wave
     static constexpr int V_PER_W = VT / 1024 / kFastWaves;
-    static constexpr int LOADS = K_PER_W + V_PER_W;          // per wave per tile
     static_assert(K_PER_W >= 1 && V_PER_W >= 1, "tile split");
 };
 
@@ -752,7 +766,7 @@ attn_fwd_fast16(KernelArgs p)
 {
     using T = Fast16<DQ, DV>;
     constexpr int BN = T::BN;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::ST * T::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -789,23 +803,32 @@ attn_fwd_fast16(KernelArgs p)
         voff[j] = c * 8 < p.D_v ? (uint32_t)(row * p.D_v + c * 8) * 2 : kOutOfRange;
     }
     const uint32_t lds_k0 = (uint32_t)__builtin_amdgcn_readfirstlane(
-        lds_address(smem) + (uint32_t)wave * T::K_PER_W * 1024);
+        lds_address(smem) + T::K_SLOT0 + (uint32_t)wave * T::K_PER_W * 1024);
     const uint32_t lds_v0 = (uint32_t)__builtin_amdgcn_readfirstlane(
-        lds_address(smem) + T::KT + (uint32_t)wave * T::V_PER_W * 1024);
-    auto issue_tile = [&](int t) {
-        const uint32_t st = (uint32_t)(t % T::ST) * T::STAGE;
+        lds_address(smem) + T::V_SLOT0 + (uint32_t)wave * T::V_PER_W * 1024);
+    auto issue_k = [&](int t) {   // K of tile t into K slot t % KS
         const uint32_t kb = (uint32_t)t * BN * p.D_qk * 2;
+        const uint32_t sl = (uint32_t)(t % T::KS) * T::KT;
+#pragma unroll
+        for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + sl + j * 1024, koff[j] + kb, rk);
+    };
+    auto issue_v = [&](int t) {   // V of tile t into V slot t % VS
         const uint32_t vb = (uint32_t)t * BN * p.D_v * 2;
+        const uint32_t sl = (uint32_t)(t % T::VS) * T::VT;
 #pragma unroll
-        for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + st + j * 1024, koff[j] + kb, rk);
-#pragma unroll
-        for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + st + j * 1024, voff[j] + vb, rv);
+        for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + sl + j * 1024, voff[j] + vb, rv);
+    };
+    // Load schedule: "iteration" j issues K(j + VS + 1) then V(j + VS - 1);
+    // iterations -VS-1 .. -1 form the prologue.  Tiles past the last are
+    // skipped.
+    auto issue_group = [&](int j, int ntiles_) {
+        if (j + T::VS + 1 >= 0 && j + T::VS + 1 < ntiles_) issue_k(j + T::VS + 1);
+        if (j + T::VS - 1 >= 0 && j + T::VS - 1 < ntiles_) issue_v(j + T::VS - 1);
     };
 
     const int ntiles = kv_tiles_for(qb, kFastBlockM, BN, p.S_q, p.S_k, CAUSAL);
 #pragma unroll
-    for (int t = 0; t < T::ST - 1; ++t)
-        if (t < ntiles) issue_tile(t);
+    for (int j = -T::VS - 1; j < 0; ++j) issue_group(j, ntiles);
 
     // ---- Q fragment (B operand of S^T = K Q^T): query qi, dims 16st + 8hh + 0..7
     u32x4 qf[DQ / 16];
@@ -819,10 +842,10 @@ attn_fwd_fast16(KernelArgs p)
         qf[st] = x;
     }
 
-    // ---- per-lane LDS read offsets (relative to a stage), computed once
+    // ---- per-lane LDS read addresses in stage 0, computed once
     // K (score A operand): row 32kb + sigma(l32), logical chunk 2st + hh.
     // The swizzle depends on the row only through bits the kb term does not
-    // touch, so the kb offset is a constant added per read.
+    // touch, so the kb offset is an immediate.
     uint32_t kro[DQ / 16];
     {
         const int krow = sigma(l32);
@@ -842,7 +865,7 @@ attn_fwd_fast16(KernelArgs p)
         for (int d = 0; d < DV / 32; ++d) {
             const int chunk = (d * 4 + (vg & 1) * 2 + (vq >> 1)) ^ vswz<T::VCH>(row);
             vro[d] = lds_address(smem) +
-                     (uint32_t)(T::KT + row * T::VROW + chunk * 16 + (vq & 1) * 8);
+                     (uint32_t)(T::V_SLOT0 + row * T::VROW + chunk * 16 + (vq & 1) * 8);
         }
     }
 
@@ -850,114 +873,138 @@ attn_fwd_fast16(KernelArgs p)
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
     const float c = p.c;
-    float m = neg_inf();
-    float l = 0.0f;
+    float m = neg_inf();   // running max of the raw scores of this query
+    float l = 0.0f;        // running sum of this lane's half of the keys
 
-    uint32_t stage_off = 0;   // byte offset of tile t's stage, rotating over ST stages
+    // S^T of the key tile staged at `so` (two 32-key blocks).
+    auto scores = [&](uint32_t so, f32x16 (&out)[2]) {
+        out[0] = f32x16{};
+        out[1] = f32x16{};
+#pragma unroll
+        for (int st = 0; st < DQ / 16; ++st) {
+            const auto *k0 = reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                lds_ptr(kro[st] + so));
+            const auto *k1 = reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
+                lds_ptr(kro[st] + so) + 32 * T::KROW);
+            out[0] = mma16<BF16>(*k0, qf[st], out[0]);
+            out[1] = mma16<BF16>(*k1, qf[st], out[1]);
+        }
+    };
+    auto lane_max = [](const f32x16 (&x)[2]) {
+        float mx = x[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
+        return mx;
+    };
+    // O^T += V^T P^T for one 32-key block kb of the tile staged at `so`.
+    auto pv_block = [&](uint32_t so, int kb, const u32x4 (&pb)[2]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int d = 0; d < DV / 32; ++d) {
+                uint32_t a[4];
+#pragma unroll
+                for (int sh = 0; sh < 2; ++sh) {
+                    const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(
+                        lds_ptr(vro[d] + so) + (kb * 32 + u * 16 + sh * 4) * T::VROW));
+                    const u32x2 xw = __builtin_bit_cast(u32x2, x);
+                    a[2 * sh] = xw.x;
+                    a[2 * sh + 1] = xw.y;
+                }
+                o[d] = mma16<BF16>(u32x4{a[0], a[1], a[2], a[3]}, pb[u], o[d]);
+            }
+    };
+    // P = 2^(s c - m c) for one 32-key block, packed to 16 bits; the row sum
+    // is taken over the f32 values so that LSE keeps f32 accuracy.
+    auto probs = [&](const f32x16 &sb, float mc, u32x4 (&pb)[2], float &rs) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float p0 = fast_exp2(__builtin_fmaf(sb[8 * u + 2 * j], c, -mc));
+                const float p1 = fast_exp2(__builtin_fmaf(sb[8 * u + 2 * j + 1], c, -mc));
+                rs += p0 + p1;
+                w[j] = pack2<BF16>(p0, p1);
+            }
+            pb[u] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+    };
+
+    // ---- prologue: scores of tile 0.  K(0) was the first load issued; every
+    // later prologue load may still be in flight when all of them exist.
+    if (ntiles > T::VS) wait_loads<(T::VS - 1) * T::LOADS + T::K_PER_W>();
+    else wait_loads<0>();
+    __syncthreads();
+    f32x16 sn[2];
+    scores(0, sn);
+    float mxn = lane_max(sn);
+
+    // ---- main loop, software pipelined: iteration t finishes tile t (softmax,
+    // P V) while the scores of tile t+1 are formed, so every phase has MFMA
+    // and VALU work from the same wave to overlap.
     for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles) wait_loads<T::LOADS>();
+        const uint32_t so = (uint32_t)(t % T::VS) * T::VT;         // V slot of tile t
+        const uint32_t so1 = (uint32_t)((t + 1) % T::KS) * T::KT;  // K slot of tile t+1
+        const int kbase = t * BN;
+        const bool active = !CAUSAL || kbase <= qw + 31;   // some key of tile t is visible
+
+        f32x16 s[2] = {sn[0], sn[1]};
+        float mx = mxn;
+        if (active) {
+            // masks: keys >= S_k; keys after the query when causal
+            const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > qw);
+            if (need_mask) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kbase + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
+                        bool ok = key < p.S_k;
+                        if (CAUSAL) ok = ok && key <= qi;
+                        s[kb][r] = ok ? s[kb][r] : neg_inf();
+                    }
+                mx = lane_max(s);
+            }
+            // running max; rescale only when a row's max grows by > 2^kTau
+            mx = max_halves(mx);
+            const bool grow = (mx - m) * c > kTau;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = fast_exp2((m - m_new) * c);
+                m = m_new;
+                l *= alpha;
+#pragma unroll
+                for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+            }
+        }
+
+        // V(t) (issued in iteration t-VS+1, after K(t+1)) must be resident.
+        // Loads issued after it: the groups of iterations t-VS+2 .. t-1, which
+        // are complete while t+VS < ntiles; near the end wait for everything.
+        // Then every wave is done with the slots of V(t-1) and K(t), which
+        // this iteration refills.
+        if (t + T::VS < ntiles) wait_loads<(T::VS - 2) * T::LOADS>();
         else wait_loads<0>();
         __syncthreads();
-        if (t + T::ST - 1 < ntiles) issue_tile(t + T::ST - 1);
+        issue_group(t, ntiles);
+        if (!active) continue;   // this and every later tile is after all rows of the wave
 
-        const uint32_t so = stage_off;
-        stage_off = (stage_off == (T::ST - 1) * T::STAGE) ? 0u : stage_off + T::STAGE;
-        const int kbase = t * BN;
-        if (CAUSAL && kbase > qw + 31) continue;   // every key of this tile is after every row
-
-        // per-tile read bases; the rest of each address is an immediate offset
-        uint32_t kaddr[DQ / 16], vaddr[DV / 32];
-#pragma unroll
-        for (int st = 0; st < DQ / 16; ++st) kaddr[st] = kro[st] + so;
-#pragma unroll
-        for (int d = 0; d < DV / 32; ++d) vaddr[d] = vro[d] + so;
-
-        // ---- scores S^T (two 32-key blocks)
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-#pragma unroll
-            for (int st = 0; st < DQ / 16; ++st) {
-                const u32x4 a =
-                    *reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
-                        lds_ptr(kaddr[st]) + kb * 32 * T::KROW);
-                s[kb] = mma16<BF16>(a, qf[st], s[kb]);
-            }
-        }
-
-        // ---- masks: keys >= S_k; keys after the query when causal
-        const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > qw);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kbase + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
-                    bool ok = key < p.S_k;
-                    if (CAUSAL) ok = ok && key <= qi;
-                    s[kb][r] = ok ? s[kb][r] : neg_inf();
-                }
-        }
-
-        // ---- running max; rescale only when a row's max grows by > 2^kTau
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = max_halves(mx);
-        const bool grow = (mx - m) * c > kTau;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float m_new = fmaxf(m, mx);
-            const float alpha = fast_exp2((m - m_new) * c);
-            m = m_new;
-            l *= alpha;
-#pragma unroll
-            for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
-        }
         const float mc = m * c;
-
-        // ---- P = 2^(s c - m c) packed to 16 bits; the row sum is taken over
-        // the f32 values so that LSE keeps f32 accuracy
-        u32x4 pf[2][2];
-        float rs0 = 0.0f, rs1 = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                uint32_t w[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][8 * u + 2 * j], c, -mc));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][8 * u + 2 * j + 1], c, -mc));
-                    rs0 += p0;
-                    rs1 += p1;
-                    w[j] = pack2<BF16>(p0, p1);
-                }
-                pf[kb][u] = u32x4{w[0], w[1], w[2], w[3]};
-            }
-        l += rs0 + rs1;
-
-        // ---- O^T += V^T P^T; the A operand comes from two transposed reads
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-#pragma unroll
-                for (int d = 0; d < DV / 32; ++d) {
-                    uint32_t a[4];
-#pragma unroll
-                    for (int sh = 0; sh < 2; ++sh) {
-                        const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4 *)(lds_ptr(vaddr[d]) + (kb * 32 + u * 16 + sh * 4) * T::VROW));
-                        const u32x2 xw = __builtin_bit_cast(u32x2, x);
-                        a[2 * sh] = xw.x;
-                        a[2 * sh + 1] = xw.y;
-                    }
-                    o[d] = mma16<BF16>(u32x4{a[0], a[1], a[2], a[3]}, pf[kb][u], o[d]);
-                }
-            }
+        float rs = 0.0f;
+        u32x4 pb0[2], pb1[2];
+        // phase A: scores of tile t+1 (garbage past the last tile, unused) || P of block 0
+        scores(so1, sn);
+        probs(s[0], mc, pb0, rs);
+        // phase B1: O += V P for block 0 || P of block 1
+        pv_block(so, 0, pb0);
+        probs(s[1], mc, pb1, rs);
+        // phase B2: O += V P for block 1 || lane max of the next scores
+        pv_block(so, 1, pb1);
+        mxn = lane_max(sn);
+        l += rs;
     }
 
     // ---- epilogue: O = O_acc / l, LSE = m*scale + ln(l)
@@ -1031,7 +1078,7 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec)
         t.waves = kFastWaves;
         t.threads = kFastThreads;
         t.block_n = F::BN;
-        t.lds_bytes = F::ST * F::BN * (t.dqk_block + t.dv_block) * 2;
+        t.lds_bytes = (F::KS * t.dqk_block + F::VS * t.dv_block) * F::BN * 2;
     } else if (dtype == TSD_F32) {
         t.block_m = kBlockM;
         t.waves = kThreads / 64;
