@@ -42,6 +42,16 @@ def parse():
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="oracle sample: every N-th query row of every head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the benchmark, run --steps launches of a plain device "
+                         "copy of this many MiB (counter calibration for HBM traffic)")
+    ap.add_argument("--record-traffic", nargs=4, metavar=("ATTN_FETCH", "ATTN_WRITE",
+                                                          "COPY_FETCH", "COPY_WRITE"),
+                    help="write the HBM traffic per launch into the stored traffic record "
+                         "from four rocprofv3 --pmc output folders (FETCH_SIZE and "
+                         "WRITE_SIZE of this benchmark, then of --copy-probe-mib)")
+    ap.add_argument("--copy-mib", type=int, default=1024,
+                    help="size the --copy-probe-mib run used (for --record-traffic)")
     return ap.parse_args()
 
 
@@ -62,6 +72,91 @@ def stored_traffic(workload: str):
     if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def copy_probe(mib: int, launches: int) -> int:
+    """Launch a plain strided device copy of `mib` MiB `launches` times.
+
+    The source is the left half of a wider f32 matrix, so the copy runs as an
+    element-wise kernel (a contiguous copy would go to the DMA engines): it
+    reads exactly `mib` MiB and writes `mib` MiB, rows aligned to 256 bytes.
+    Its FETCH_SIZE / WRITE_SIZE readings calibrate the counters."""
+    import torch
+
+    cols = 16384
+    rows = mib * (1 << 20) // (4 * cols)
+    dev = torch.device("cuda:0")
+    src = torch.empty((rows, 2 * cols), dtype=torch.float32, device=dev)
+    dst = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    for _ in range(launches):
+        dst.copy_(src[:, :cols])
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": rows * cols * 4, "launches": launches}), flush=True)
+    return 0
+
+
+def pmc_per_dispatch(folder: str, counter: str, name_filter) -> float:
+    """Mean of one counter over the dispatches whose kernel name passes the
+    filter, from a rocprofv3 --pmc --output-format csv folder (KiB for the
+    *_SIZE counters)."""
+    import csv
+    import glob
+
+    vals = []
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter and name_filter(row["Kernel_Name"]):
+                    vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows in {folder}")
+    return sum(vals) / len(vals)
+
+
+def record_traffic(args) -> int:
+    """Scale the attention kernel's FETCH_SIZE and WRITE_SIZE by what the same
+    counters read for the copy probe (bytes known exactly) and store the
+    result, keyed by workload and kernel source hash."""
+    from tiled_scaled_dot_amd.workloads import HEADLINE, WORKLOADS
+
+    name = args.workload or HEADLINE
+    w = WORKLOADS[name]
+    a_fetch, a_write, c_fetch, c_write = args.record_traffic
+    is_attn = lambda k: "attn_fwd" in k
+    is_copy = lambda k: "attn_fwd" not in k
+    copy_bytes = (args.copy_mib << 20) // (4 * 16384) * 16384 * 4
+    fetch_kib = pmc_per_dispatch(a_fetch, "FETCH_SIZE", is_attn)
+    write_kib = pmc_per_dispatch(a_write, "WRITE_SIZE", is_attn)
+    cf_kib = pmc_per_dispatch(c_fetch, "FETCH_SIZE", is_copy)
+    cw_kib = pmc_per_dispatch(c_write, "WRITE_SIZE", is_copy)
+    f_scale = copy_bytes / (cf_kib * 1024.0)
+    w_scale = copy_bytes / (cw_kib * 1024.0)
+    read_b = fetch_kib * 1024.0 * f_scale
+    write_b = write_kib * 1024.0 * w_scale
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec[name] = {
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "hbm_bytes_per_launch": round(read_b + write_b),
+        "read_bytes": round(read_b),
+        "write_bytes": round(write_b),
+        "algorithmic_bytes": w.min_bytes(),
+        "fetch_size_kib": fetch_kib,
+        "write_size_kib": write_kib,
+        "copy_probe_bytes": copy_bytes,
+        "copy_fetch_size_kib": cf_kib,
+        "copy_write_size_kib": cw_kib,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(rec[name]))
+    return 0
 
 
 def cpu_baseline(w, q, k, v, stride: int):
@@ -106,6 +201,11 @@ def main():
               "the path shards per (batch, head) slice with no exchange, but no multi-GPU "
               "run is part of it.", file=sys.stderr)
         return 2
+
+    if args.record_traffic:
+        return record_traffic(args)
+    if args.copy_probe_mib:
+        return copy_probe(args.copy_probe_mib, args.steps)
 
     import torch
 

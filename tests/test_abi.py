@@ -149,11 +149,17 @@ def test_plan_for_workloads(lib, name):
         # generic kernel: 4 waves x 32 rows, 32-key tiles, two LDS stages
         assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (128, 256, 4, 32)
         assert plan.lds_bytes <= 64 * 1024
+    elif plan.dqk_block == 64 and plan.dv_block == 64:
+        # LDS-direct kernel, narrow heads: 4 waves x 32 rows, 64-key tiles,
+        # K and V rings of 2 slots each, three workgroups per CU
+        assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (128, 256, 4, 64)
+        assert plan.lds_bytes == (2 * 64 + 2 * 64) * 64 * 2
+        assert 3 * plan.lds_bytes <= 160 * 1024
     else:
-        # LDS-direct kernel: 8 waves x 32 rows, 64-key tiles, K ring of 4 slots
-        # and V ring of 3 slots
+        # LDS-direct kernel, wide heads: 8 waves x 32 rows, 64-key tiles, K
+        # ring of 4 slots and V ring of 2 slots
         assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (256, 512, 8, 64)
-        assert plan.lds_bytes == (4 * plan.dqk_block + 3 * plan.dv_block) * 64 * 2
+        assert plan.lds_bytes == (4 * plan.dqk_block + 2 * plan.dv_block) * 64 * 2
         assert plan.lds_bytes <= 160 * 1024
     bm = plan.block_m
     assert plan.dqk_block >= w.D_qk and plan.dv_block >= w.D_v

@@ -101,6 +101,8 @@ EDGE = [
     (1, 1, 150, 150, 64, 64, -0.3),
     (1, 1, 150, 150, 64, 64, 0.0),
     (1, 1, 150, 150, 32, 32, 0.6),
+    (1, 4, 1500, 1500, 64, 64, 0.125),
+    (2, 2, 700, 1100, 32, 64, 0.2),
 ]
 
 
@@ -116,6 +118,48 @@ def test_edge_shapes(case, causal, dtype):
     o, lse = run_gpu(q, k, v, scale, causal)
     o_ref, lse_ref = run_oracle(q, k, v, scale, causal)
     check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"{case} c={causal} {dtype}")
+
+
+# ------------------------------------------- masked keys and the running max
+def _aligned_inputs(S_q, S_k, D, key_score, dtype, seed):
+    """Q rows all equal to u = (1/8, ..., 1/8) and K row j = u * a_j, so that
+    with D = 64 and scale 1 the score of every query against key j is a_j;
+    V is N(0, 1)."""
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    u = torch.full((D,), 1.0 / 8.0)
+    a = torch.tensor([key_score(j) for j in range(S_k)], dtype=torch.float64).float()
+    q = u.expand(1, 1, S_q, D).clone().to(dt)
+    k = (a[:, None] * u[None, :] * (64.0 / D)).reshape(1, 1, S_k, D).to(dt)
+    v = torch.randn((1, 1, S_k, D), generator=g).to(dt)
+    return q, k, v
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("S_q,S_k", [(700, 700), (700, 650), (130, 1000)])
+def test_hidden_keys_never_set_the_max(dtype, S_q, S_k):
+    """Causal: scores rise by 2 per key inside every aligned run of 128 keys,
+    so for a query at the start of a 64-key tile a later key of that tile
+    that leaked into the running max would push its visible exp(s - m)
+    below the f32 range (O and LSE would be NaN or far off)."""
+    print(f"[case] rising scores causal {S_q}x{S_k} {dtype}", flush=True)
+    q, k, v = _aligned_inputs(S_q, S_k, 64, lambda j: 2.0 * (j % 128), dtype, 11)
+    o, lse = run_gpu(q, k, v, 1.0, True)
+    o_ref, lse_ref = run_oracle(q, k, v, 1.0, True)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"rising causal {S_q}x{S_k} {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("S_q,S_k", [(300, 1000), (300, 97), (64, 33)])
+def test_keys_past_sk_never_set_the_max(dtype, S_q, S_k):
+    """Non-causal, every real score between -206 and -200: the zero-filled
+    rows past S_k in the last key tile would score 0 and, if they reached the
+    running max, underflow every exp(s - m) to zero."""
+    print(f"[case] negative scores {S_q}x{S_k} {dtype}", flush=True)
+    q, k, v = _aligned_inputs(S_q, S_k, 64, lambda j: -200.0 - (j % 7), dtype, 12)
+    o, lse = run_gpu(q, k, v, 1.0, False)
+    o_ref, lse_ref = run_oracle(q, k, v, 1.0, False)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"negative {S_q}x{S_k} {dtype}")
 
 
 # ------------------------------------------------ writes, determinism, streams

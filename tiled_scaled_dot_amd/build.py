@@ -33,7 +33,8 @@ def hipcc() -> str:
 def build(output: str = LIBRARY, extra_flags=None, verbose: bool = False) -> str:
     """Compile every HIP source into one shared library (always rebuilds)."""
     objs = []
-    tmpdir = os.path.join(PKG, "_build")
+    # one object folder per output, so that several builds may run at once
+    tmpdir = os.path.join(PKG, "_build", os.path.splitext(os.path.basename(output))[0])
     os.makedirs(tmpdir, exist_ok=True)
     flags = HIPCC_FLAGS + list(extra_flags or [])
     procs = []

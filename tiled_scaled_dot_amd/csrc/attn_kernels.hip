@@ -29,6 +29,8 @@
 //     v_mfma_f32_32x32x2_f32.  Accumulation is always f32.
 //   * exp is computed as exp2 with log2(e) folded into the scale.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "launch.h"
@@ -663,17 +665,37 @@ attn_fwd_32(KernelArgs p)
 //   * O and LSE are written with buffer stores; stores outside the slice are
 //     dropped by the hardware range check.
 // ====================================================================
-#ifndef TSD_FAST_WAVES
-#define TSD_FAST_WAVES 8
+// Launch shapes of the fast kernel, chosen per head width (measured on
+// MI355X): with 128-wide heads a wave needs ~210 VGPRs, so two waves per
+// SIMD (8-wave workgroups, one per CU); with 64-wide heads it fits in ~160,
+// and three 4-wave workgroups per CU (three waves per SIMD) hide more
+// latency.  K and V tiles sit in LDS ring buffers of kslots / vslots tiles;
+// the main loop is unrolled by kslots so every ring slot is a compile-time
+// offset (vslots divides kslots).
+struct FastShape {
+    int waves;    // waves per workgroup (rows per workgroup = 32 * waves)
+    int kslots;   // K ring size (the unroll factor of the main loop)
+    int vslots;   // V ring size
+    int occ;      // waves per SIMD the kernel is compiled for
+};
+#ifndef TSD_WIDE_KSLOTS
+#define TSD_WIDE_KSLOTS 4
 #endif
-#ifndef TSD_FAST_VSLOTS
-#define TSD_FAST_VSLOTS 3
+#ifndef TSD_WIDE_VSLOTS
+#define TSD_WIDE_VSLOTS 2
 #endif
-constexpr int kFastWaves = TSD_FAST_WAVES;   // waves per workgroup (4 or 8)
-constexpr int kFastThreads = kFastWaves * 64;
-constexpr int kFastBlockM = kFastWaves * 32;
-constexpr int kVSlots = TSD_FAST_VSLOTS;     // V ring size; the K ring has one slot more
-static_assert(kVSlots >= 2 && kVSlots <= 4, "V ring size");
+#ifndef TSD_NARROW_KSLOTS
+#define TSD_NARROW_KSLOTS 2
+#endif
+#ifndef TSD_NARROW_VSLOTS
+#define TSD_NARROW_VSLOTS 2
+#endif
+constexpr FastShape kShapeWide = {8, TSD_WIDE_KSLOTS, TSD_WIDE_VSLOTS, 2};
+constexpr FastShape kShapeNarrow = {4, TSD_NARROW_KSLOTS, TSD_NARROW_VSLOTS, 3};
+constexpr FastShape fast_shape(int dq, int dv)
+{
+    return (dq <= 64 && dv <= 64) ? kShapeNarrow : kShapeWide;
+}
 constexpr float kTau = 8.0f;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // above any slice size (< 2^31 bytes)
 constexpr int kBufferConfig = 0x00020000;       // raw buffer, 32-bit data format
@@ -681,21 +703,86 @@ constexpr int kBufferConfig = 0x00020000;       // raw buffer, 32-bit data forma
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+template <int N>
+using IC = std::integral_constant<int, N>;
+
+// f(IC<B>{}), f(IC<B+1>{}), ..., f(IC<E-1>{})
+template <int B, int E, typename F>
+__device__ __attribute__((always_inline)) inline void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(IC<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Instruction interleaving of one main-loop iteration.  A wave issues in
+// order, so the compiler's default order (a run of score MFMAs separated by
+// LDS waits, then a run of exp/convert VALU) leaves the matrix and vector
+// pipes taking turns.  These scheduling groups ask for each MFMA to be
+// followed by a few VALU instructions and the next LDS reads, keeping
+// operands a few reads ahead.  Masks: 0x8 MFMA, 0x2 VALU, 0x100 LDS read.
+#ifndef TSD_SCHED
+#define TSD_SCHED 1
+#endif
+#ifndef TSD_SCHED_VALU
+#define TSD_SCHED_VALU 3
+#endif
+#ifndef TSD_SCHED_LEAD
+#define TSD_SCHED_LEAD 4
+#endif
+template <int MASK, int N>
+__device__ __attribute__((always_inline)) inline void sched_group()
+{
+    if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+// NS score MFMAs (one K read each), then NP P V MFMAs (two transposed V
+// reads each).
+template <int NS, int NP>
+__device__ __attribute__((always_inline)) inline void schedule_iteration()
+{
+    if constexpr (TSD_SCHED) {
+        constexpr int LEAD = TSD_SCHED_LEAD < NS ? TSD_SCHED_LEAD : NS;
+        constexpr int VA = TSD_SCHED_VALU;
+        sched_group<0x100, LEAD>();
+        sched_group<0x002, 2 * VA>();
+        static_for<0, NS>([&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            sched_group<0x008, 1>();
+            sched_group<0x100, (i + LEAD < NS) ? 1 : 2>();
+            sched_group<0x002, VA>();
+        });
+        static_for<0, NP>([&](auto ic) __attribute__((always_inline)) {
+            sched_group<0x008, 1>();
+            sched_group<0x100, 2>();
+            sched_group<0x002, VA>();
+        });
+    }
+}
+
 template <int DQ, int DV>
 struct Fast16 {
+    static constexpr FastShape SH = fast_shape(DQ, DV);
+    static constexpr int NW = SH.waves, THREADS = 64 * SH.waves, BM = 32 * SH.waves;
     static constexpr int BN = 64;
     static constexpr int KROW = DQ * 2, VROW = DV * 2; // bytes per row in LDS
     static constexpr int KCH = DQ / 8, VCH = DV / 8;   // 16-byte chunks per row
     static constexpr int KT = BN * KROW, VT = BN * VROW;
-    // Ring buffers: VS slots for V and VS+1 for K.  K of tile t+1 is read in
-    // the same iteration as V of tile t, so K runs one tile ahead of V.
-    static constexpr int VS = kVSlots, KS = kVSlots + 1;
+    // Ring buffers of KS K tiles and VS V tiles.  Iteration t reads K(t+1)
+    // (scores of the next tile) and V(t); after its barrier it refills the
+    // slots of K(t) and V(t-1) with K(t+KS) and V(t+VS-1).
+    static constexpr int KS = SH.kslots, VS = SH.vslots, U = SH.kslots;
     static constexpr int K_SLOT0 = 0, V_SLOT0 = KS * KT;
     static constexpr int LDS_BYTES = KS * KT + VS * VT;
-    static constexpr int LOADS = KT / 1024 / kFastWaves + VT / 1024 / kFastWaves;
-    static constexpr int K_PER_W = KT / 1024 / kFastWaves;   // 1 KB load instructions per wave
-    static constexpr int V_PER_W = VT / 1024 / kFastWaves;
-    static_assert(K_PER_W >= 1 && V_PER_W >= 1, "tile split");
+    static constexpr int K_PER_W = KT / 1024 / NW;   // 1 KB load instructions per wave
+    static constexpr int V_PER_W = VT / 1024 / NW;
+    static constexpr int LOADS = K_PER_W + V_PER_W;  // per wave per tile
+    static_assert(K_PER_W >= 1 && V_PER_W >= 1 && KT % (1024 * NW) == 0 &&
+                      VT % (1024 * NW) == 0, "tile split");
+    static_assert(VS >= 2 && KS >= VS && KS % VS == 0 && (KS == 2 || KS == 4), "ring sizes");
+    // ds_read immediate offsets are 16-bit: every K slot and every V slot
+    // must be reachable from one base register each.
+    static_assert(KS * KT <= 65536 && VS * VT <= 65536, "ring too large for immediates");
 };
 
 // LDS swizzles for the fast kernel.  gfx950's LDS has 64 banks of 4 bytes
@@ -726,6 +813,16 @@ __device__ inline u32x4 rsrc_words(const void *base, uint32_t bytes)
     return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b),
                  (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)),
                  (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kBufferConfig};
+}
+
+// The descriptor advanced by `off` bytes (off <= its range): base + off,
+// range - off.  All words are wave-uniform.
+__device__ __attribute__((always_inline)) inline u32x4 tile_rsrc(const u32x4 &r, uint32_t off)
+{
+    const uint64_t base = ((uint64_t)r.y << 32 | r.x) + off;
+    return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(r.z - off), r.w};
 }
 
 // One wave instruction: 64 lanes x 16 bytes from the buffer (lane offset
@@ -760,8 +857,10 @@ __device__ inline void wait_loads()
 }
 
 template <int DQ, int DV, bool CAUSAL, bool BF16>
-__global__ void __attribute__((amdgpu_flat_work_group_size(kFastThreads, kFastThreads),
-                               amdgpu_waves_per_eu(2, 2)))
+__global__ void __attribute__((amdgpu_flat_work_group_size(Fast16<DQ, DV>::THREADS,
+                                                           Fast16<DQ, DV>::THREADS),
+                               amdgpu_waves_per_eu(Fast16<DQ, DV>::SH.occ,
+                                                   Fast16<DQ, DV>::SH.occ)))
 attn_fwd_fast16(KernelArgs p)
 {
     using T = Fast16<DQ, DV>;
@@ -775,7 +874,7 @@ attn_fwd_fast16(KernelArgs p)
 
     int32_t qb, slice;
     map_block((int32_t)blockIdx.x, p.q_blocks, p.slices, p.order, p.per_xcd, CAUSAL, qb, slice);
-    const int q0 = qb * kFastBlockM;
+    const int q0 = qb * T::BM;
     const int qw = q0 + wave * 32;          // first query row of this wave
     const int qi = qw + l32;                // this lane's query row
 
@@ -806,29 +905,34 @@ attn_fwd_fast16(KernelArgs p)
         lds_address(smem) + T::K_SLOT0 + (uint32_t)wave * T::K_PER_W * 1024);
     const uint32_t lds_v0 = (uint32_t)__builtin_amdgcn_readfirstlane(
         lds_address(smem) + T::V_SLOT0 + (uint32_t)wave * T::V_PER_W * 1024);
-    auto issue_k = [&](int t) {   // K of tile t into K slot t % KS
-        const uint32_t kb = (uint32_t)t * BN * p.D_qk * 2;
-        const uint32_t sl = (uint32_t)(t % T::KS) * T::KT;
+    // K(t) into K slot t % KS and V(t) into V slot t % VS; the slot is a
+    // compile-time constant at every call.
+    // The tile's offset moves the descriptor's base (and shrinks its range)
+    // in scalar registers, so the per-lane offsets stay fixed and the range
+    // check still drops rows past the slice.
+    auto issue_k = [&](int t, auto slot_c) __attribute__((always_inline)) {
+        constexpr uint32_t sl = decltype(slot_c)::value * T::KT;
+        const u32x4 r = tile_rsrc(rk, (uint32_t)t * BN * p.D_qk * 2);
 #pragma unroll
-        for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + sl + j * 1024, koff[j] + kb, rk);
+        for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + sl + j * 1024, koff[j], r);
     };
-    auto issue_v = [&](int t) {   // V of tile t into V slot t % VS
-        const uint32_t vb = (uint32_t)t * BN * p.D_v * 2;
-        const uint32_t sl = (uint32_t)(t % T::VS) * T::VT;
+    auto issue_v = [&](int t, auto slot_c) __attribute__((always_inline)) {
+        constexpr uint32_t sl = decltype(slot_c)::value * T::VT;
+        const u32x4 r = tile_rsrc(rv, (uint32_t)t * BN * p.D_v * 2);
 #pragma unroll
-        for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + sl + j * 1024, voff[j] + vb, rv);
-    };
-    // Load schedule: "iteration" j issues K(j + VS + 1) then V(j + VS - 1);
-    // iterations -VS-1 .. -1 form the prologue.  Tiles past the last are
-    // skipped.
-    auto issue_group = [&](int j, int ntiles_) {
-        if (j + T::VS + 1 >= 0 && j + T::VS + 1 < ntiles_) issue_k(j + T::VS + 1);
-        if (j + T::VS - 1 >= 0 && j + T::VS - 1 < ntiles_) issue_v(j + T::VS - 1);
+        for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + sl + j * 1024, voff[j], r);
     };
 
-    const int ntiles = kv_tiles_for(qb, kFastBlockM, BN, p.S_q, p.S_k, CAUSAL);
-#pragma unroll
-    for (int j = -T::VS - 1; j < 0; ++j) issue_group(j, ntiles);
+    const int ntiles = kv_tiles_for(qb, T::BM, BN, p.S_q, p.S_k, CAUSAL);
+    // Prologue: K(0 .. KS-1) and V(0 .. VS-2) in the order the main loop
+    // would have issued them (K(j) before V(j-1)), K(0) first.
+    issue_k(0, IC<0>{});
+    static_for<1, T::KS>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        if (j < ntiles) issue_k(j, IC<j>{});
+        if constexpr (j - 1 < T::VS - 1)
+            if (j - 1 < ntiles) issue_v(j - 1, IC<j - 1>{});
+    });
 
     // ---- Q fragment (B operand of S^T = K Q^T): query qi, dims 16st + 8hh + 0..7
     u32x4 qf[DQ / 16];
@@ -877,7 +981,7 @@ attn_fwd_fast16(KernelArgs p)
     float l = 0.0f;        // running sum of this lane's half of the keys
 
     // S^T of the key tile staged at `so` (two 32-key blocks).
-    auto scores = [&](uint32_t so, f32x16 (&out)[2]) {
+    auto scores = [&](uint32_t so, f32x16 (&out)[2]) __attribute__((always_inline)) {
         out[0] = f32x16{};
         out[1] = f32x16{};
 #pragma unroll
@@ -890,7 +994,7 @@ attn_fwd_fast16(KernelArgs p)
             out[1] = mma16<BF16>(*k1, qf[st], out[1]);
         }
     };
-    auto lane_max = [](const f32x16 (&x)[2]) {
+    auto lane_max = [](const f32x16 (&x)[2]) __attribute__((always_inline)) {
         float mx = x[0][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -899,7 +1003,7 @@ attn_fwd_fast16(KernelArgs p)
         return mx;
     };
     // O^T += V^T P^T for one 32-key block kb of the tile staged at `so`.
-    auto pv_block = [&](uint32_t so, int kb, const u32x4 (&pb)[2]) {
+    auto pv_block = [&](uint32_t so, int kb, const u32x4 (&pb)[2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -918,7 +1022,7 @@ attn_fwd_fast16(KernelArgs p)
     };
     // P = 2^(s c - m c) for one 32-key block, packed to 16 bits; the row sum
     // is taken over the f32 values so that LSE keeps f32 accuracy.
-    auto probs = [&](const f32x16 &sb, float mc, u32x4 (&pb)[2], float &rs) {
+    auto probs = [&](const f32x16 &sb, float mc, u32x4 (&pb)[2], float &rs) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             uint32_t w[4];
@@ -934,38 +1038,47 @@ attn_fwd_fast16(KernelArgs p)
     };
 
     // ---- prologue: scores of tile 0.  K(0) was the first load issued; every
-    // later prologue load may still be in flight when all of them exist.
-    if (ntiles > T::VS) wait_loads<(T::VS - 1) * T::LOADS + T::K_PER_W>();
+    // other prologue load may still be in flight when all of them exist.
+    if (ntiles >= T::KS) wait_loads<(T::KS - 1) * T::K_PER_W + (T::VS - 1) * T::V_PER_W>();
     else wait_loads<0>();
     __syncthreads();
-    f32x16 sn[2];
-    scores(0, sn);
-    float mxn = lane_max(sn);
+    f32x16 sc[2][2];     // scores of tiles t and t+1, alternating by parity
+    float mxs[2];        // their lane maxima
+    scores(0, sc[0]);
+    mxs[0] = lane_max(sc[0]);
 
-    // ---- main loop, software pipelined: iteration t finishes tile t (softmax,
-    // P V) while the scores of tile t+1 are formed, so every phase has MFMA
-    // and VALU work from the same wave to overlap.
-    for (int t = 0; t < ntiles; ++t) {
-        const uint32_t so = (uint32_t)(t % T::VS) * T::VT;         // V slot of tile t
-        const uint32_t so1 = (uint32_t)((t + 1) % T::KS) * T::KT;  // K slot of tile t+1
+    // ---- one iteration of the main loop, software pipelined: iteration t
+    // finishes tile t (softmax, P V) while the scores of tile t+1 are formed,
+    // so every phase has MFMA and VALU work from the same wave to overlap.
+    // u = t % KS is a compile-time constant, so ring slots are immediates and
+    // the score registers alternate without copies.
+    auto step = [&](int t, auto uc) __attribute__((always_inline)) {
+        constexpr int u = decltype(uc)::value;
+        constexpr uint32_t so = (uint32_t)(u % T::VS) * T::VT;          // V slot of tile t
+        constexpr uint32_t so1 = (uint32_t)((u + 1) % T::KS) * T::KT;   // K slot of tile t+1
+        f32x16(&s)[2] = sc[u & 1];
+        f32x16(&sn)[2] = sc[(u + 1) & 1];
         const int kbase = t * BN;
         const bool active = !CAUSAL || kbase <= qw + 31;   // some key of tile t is visible
 
-        f32x16 s[2] = {sn[0], sn[1]};
-        float mx = mxn;
+        float mx = mxs[u & 1];
         if (active) {
             // masks: keys >= S_k; keys after the query when causal
             const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > qw);
             if (need_mask) {
+                // Register r of block kb holds key kbase + hh*8 + kb*32 +
+                // (r/8)*16 + r%8; it is kept when that key is < S_k and,
+                // causal, <= the query: one per-lane limit against
+                // compile-time offsets.
+                int lim = p.S_k - 1;
+                if (CAUSAL) lim = min(lim, qi);
+                lim -= kbase + hh * 8;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = kbase + kb * 32 + (r >> 3) * 16 + hh * 8 + (r & 7);
-                        bool ok = key < p.S_k;
-                        if (CAUSAL) ok = ok && key <= qi;
-                        s[kb][r] = ok ? s[kb][r] : neg_inf();
-                    }
+                    for (int r = 0; r < 16; ++r)
+                        s[kb][r] = (kb * 32 + (r >> 3) * 16 + (r & 7)) <= lim ? s[kb][r]
+                                                                            : neg_inf();
                 mx = lane_max(s);
             }
             // running max; rescale only when a row's max grows by > 2^kTau
@@ -981,16 +1094,17 @@ attn_fwd_fast16(KernelArgs p)
             }
         }
 
-        // V(t) (issued in iteration t-VS+1, after K(t+1)) must be resident.
-        // Loads issued after it: the groups of iterations t-VS+2 .. t-1, which
-        // are complete while t+VS < ntiles; near the end wait for everything.
-        // Then every wave is done with the slots of V(t-1) and K(t), which
-        // this iteration refills.
-        if (t + T::VS < ntiles) wait_loads<(T::VS - 2) * T::LOADS>();
+        // V(t) (the last load of iteration t-VS+1) must be resident; K(t+1)
+        // was issued no later.  Loads issued after V(t): the groups of
+        // iterations t-VS+2 .. t-1, all full while t+KS-1 < ntiles; near the
+        // end wait for everything.  After the barrier every wave is done with
+        // the slots of K(t) and V(t-1), which this iteration refills.
+        if (t + T::KS - 1 < ntiles) wait_loads<(T::VS - 2) * T::LOADS>();
         else wait_loads<0>();
         __syncthreads();
-        issue_group(t, ntiles);
-        if (!active) continue;   // this and every later tile is after all rows of the wave
+        if (t + T::KS < ntiles) issue_k(t + T::KS, IC<u % T::KS>{});
+        if (t + T::VS - 1 < ntiles) issue_v(t + T::VS - 1, IC<(u + T::VS - 1) % T::VS>{});
+        if (!active) return;   // this and every later tile is after all rows of the wave
 
         const float mc = m * c;
         float rs = 0.0f;
@@ -1003,8 +1117,21 @@ attn_fwd_fast16(KernelArgs p)
         probs(s[1], mc, pb1, rs);
         // phase B2: O += V P for block 1 || lane max of the next scores
         pv_block(so, 1, pb1);
-        mxn = lane_max(sn);
+        mxs[(u + 1) & 1] = lane_max(sn);
         l += rs;
+        schedule_iteration<2 * (DQ / 16), 4 * (DV / 32)>();
+    };
+
+    for (int t0 = 0; t0 < ntiles; t0 += T::U) {
+        step(t0, IC<0>{});
+        if (t0 + 1 >= ntiles) break;
+        step(t0 + 1, IC<1>{});
+        if constexpr (T::U == 4) {
+            if (t0 + 2 >= ntiles) break;
+            step(t0 + 2, IC<2>{});
+            if (t0 + 3 >= ntiles) break;
+            step(t0 + 3, IC<3>{});
+        }
     }
 
     // ---- epilogue: O = O_acc / l, LSE = m*scale + ln(l)
@@ -1043,11 +1170,12 @@ template <int DQ, int DV>
 hipError_t dispatch_fast(int dtype, bool causal, int64_t grid, const KernelArgs &a,
                          hipStream_t s)
 {
+    constexpr int threads = Fast16<DQ, DV>::THREADS;
     if (dtype == TSD_BF16)
-        return causal ? launch(attn_fwd_fast16<DQ, DV, true, true>, grid, a, s, kFastThreads)
-                      : launch(attn_fwd_fast16<DQ, DV, false, true>, grid, a, s, kFastThreads);
-    return causal ? launch(attn_fwd_fast16<DQ, DV, true, false>, grid, a, s, kFastThreads)
-                  : launch(attn_fwd_fast16<DQ, DV, false, false>, grid, a, s, kFastThreads);
+        return causal ? launch(attn_fwd_fast16<DQ, DV, true, true>, grid, a, s, threads)
+                      : launch(attn_fwd_fast16<DQ, DV, false, true>, grid, a, s, threads);
+    return causal ? launch(attn_fwd_fast16<DQ, DV, true, false>, grid, a, s, threads)
+                  : launch(attn_fwd_fast16<DQ, DV, false, false>, grid, a, s, threads);
 }
 
 template <int DQ, int DV>
@@ -1073,12 +1201,12 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec)
     t.dv_block = pad_dim(D_v);
     t.fast = dtype != TSD_F32 && vec;
     if (t.fast) {
-        using F = Fast16<128, 128>;
-        t.block_m = kFastBlockM;
-        t.waves = kFastWaves;
-        t.threads = kFastThreads;
-        t.block_n = F::BN;
-        t.lds_bytes = (F::KS * t.dqk_block + F::VS * t.dv_block) * F::BN * 2;
+        const FastShape sh = fast_shape(t.dqk_block, t.dv_block);
+        t.block_m = 32 * sh.waves;
+        t.waves = sh.waves;
+        t.threads = 64 * sh.waves;
+        t.block_n = 64;
+        t.lds_bytes = (sh.kslots * t.dqk_block + sh.vslots * t.dv_block) * 64 * 2;
     } else if (dtype == TSD_F32) {
         t.block_m = kBlockM;
         t.waves = kThreads / 64;
