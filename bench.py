@@ -37,7 +37,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="oracle sample: every N-th query row of every head")
