@@ -71,11 +71,15 @@ __device__ inline void swap32(float x, float &a, float &b)
     a = __builtin_bit_cast(float, (uint32_t)r[0]);
     b = __builtin_bit_cast(float, (uint32_t)r[1]);
 }
+// IEEE maximum (NaN-propagating): lowers to v_maximum3_f32 without the
+// canonicalising copies fmaxf needs.
+__device__ inline float fmax_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ inline float max_halves(float x)
 {
     float a, b;
     swap32(x, a, b);
-    return fmaxf(a, b);
+    return fmax_nan(a, b);
 }
 __device__ inline float sum_halves(float x)
 {
@@ -999,7 +1003,7 @@ attn_fwd_fast16(KernelArgs p)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kb][r]);
+            for (int r = 0; r < 16; ++r) mx = fmax_nan(mx, x[kb][r]);
         return mx;
     };
     // O^T += V^T P^T for one 32-key block kb of the tile staged at `so`.
@@ -1043,9 +1047,9 @@ attn_fwd_fast16(KernelArgs p)
     else wait_loads<0>();
     __syncthreads();
     f32x16 sc[2][2];     // scores of tiles t and t+1, alternating by parity
-    float mxs[2];        // their lane maxima
+    float mxs[2];        // their row maxima (both lane halves)
     scores(0, sc[0]);
-    mxs[0] = lane_max(sc[0]);
+    mxs[0] = max_halves(lane_max(sc[0]));
 
     // ---- one iteration of the main loop, software pipelined: iteration t
     // finishes tile t (softmax, P V) while the scores of tile t+1 are formed,
@@ -1079,10 +1083,9 @@ attn_fwd_fast16(KernelArgs p)
                     for (int r = 0; r < 16; ++r)
                         s[kb][r] = (kb * 32 + (r >> 3) * 16 + (r & 7)) <= lim ? s[kb][r]
                                                                             : neg_inf();
-                mx = lane_max(s);
+                mx = max_halves(lane_max(s));
             }
             // running max; rescale only when a row's max grows by > 2^kTau
-            mx = max_halves(mx);
             const bool grow = (mx - m) * c > kTau;
             if (__builtin_amdgcn_ballot_w64(grow) != 0) {
                 const float m_new = fmaxf(m, mx);
@@ -1117,7 +1120,7 @@ attn_fwd_fast16(KernelArgs p)
         probs(s[1], mc, pb1, rs);
         // phase B2: O += V P for block 1 || lane max of the next scores
         pv_block(so, 1, pb1);
-        mxs[(u + 1) & 1] = lane_max(sn);
+        mxs[(u + 1) & 1] = max_halves(lane_max(sn));
         l += rs;
         schedule_iteration<2 * (DQ / 16), 4 * (DV / 32)>();
     };
