@@ -159,6 +159,33 @@ def record_traffic(args) -> int:
     return 0
 
 
+def measure_sclk(step, torch, limit_s: float = 15.0):
+    """Shader clock (MHz) while `step` runs back to back: rocm-smi is started
+    as a child process and the step is launched until it has answered.  The
+    rated peak assumes 2.4 GHz; under this load the clock sits lower.
+    Returns None where rocm-smi is not available."""
+    import re
+    import subprocess
+
+    try:
+        proc = subprocess.Popen(["rocm-smi", "--showclocks"], stdout=subprocess.PIPE,
+                                stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.perf_counter()
+    while proc.poll() is None and time.perf_counter() - t0 < limit_s:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    try:
+        out = proc.communicate(timeout=max(1.0, limit_s - (time.perf_counter() - t0)))[0]
+    except subprocess.TimeoutExpired:
+        proc.kill()
+        return None
+    m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", out, flags=re.I)
+    return float(m.group(1)) if m else None
+
+
 def cpu_baseline(w, q, k, v, stride: int):
     import numpy as np
 
@@ -238,6 +265,7 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    sclk_mhz = measure_sclk(step, torch)
 
     kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
     ms_per_step = wall * 1e3 / args.steps
@@ -268,6 +296,12 @@ def main():
                        f"seed {w.seed}" if w.dist == "normal" else f"{w.dist}(-1,1), seed {w.seed}"),
             "flops_per_step": flops,
             "pct_of_mfma_peak": round(100.0 * achieved / peak, 2),
+            # the rated peak assumes 2.4 GHz; the clock read while the same
+            # step runs back to back after the timed steps gives the peak at
+            # the clock the kernel actually runs at
+            "sclk_mhz": sclk_mhz,
+            "pct_of_mfma_peak_at_sclk": (round(100.0 * achieved / (peak * sclk_mhz / 2400.0), 2)
+                                         if sclk_mhz else None),
             "device": torch.cuda.get_device_name(dev),
             "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
         },

@@ -1048,8 +1048,10 @@ attn_fwd_fast16(KernelArgs p)
     __syncthreads();
     f32x16 sc[2][2];     // scores of tiles t and t+1, alternating by parity
     float mxs[2];        // their row maxima (both lane halves)
+    bool grows[2];       // some row's max exceeds m by more than 2^kTau (unmasked tiles)
     scores(0, sc[0]);
     mxs[0] = max_halves(lane_max(sc[0]));
+    grows[0] = true;     // m is still -inf
 
     // ---- one iteration of the main loop, software pipelined: iteration t
     // finishes tile t (softmax, P V) while the scores of tile t+1 are formed,
@@ -1066,6 +1068,7 @@ attn_fwd_fast16(KernelArgs p)
         const bool active = !CAUSAL || kbase <= qw + 31;   // some key of tile t is visible
 
         float mx = mxs[u & 1];
+        bool grow_any = grows[u & 1];
         if (active) {
             // masks: keys >= S_k; keys after the query when causal
             const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > qw);
@@ -1084,10 +1087,10 @@ attn_fwd_fast16(KernelArgs p)
                         s[kb][r] = (kb * 32 + (r >> 3) * 16 + (r & 7)) <= lim ? s[kb][r]
                                                                             : neg_inf();
                 mx = max_halves(lane_max(s));
+                grow_any = __builtin_amdgcn_ballot_w64((mx - m) * c > kTau) != 0;
             }
             // running max; rescale only when a row's max grows by > 2^kTau
-            const bool grow = (mx - m) * c > kTau;
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            if (grow_any) {
                 const float m_new = fmaxf(m, mx);
                 const float alpha = fast_exp2((m - m_new) * c);
                 m = m_new;
@@ -1120,7 +1123,10 @@ attn_fwd_fast16(KernelArgs p)
         probs(s[1], mc, pb1, rs);
         // phase B2: O += V P for block 1 || lane max of the next scores
         pv_block(so, 1, pb1);
+        // the next tile's row max and its rescale decision, decided here
+        // beside the P V MFMAs (m no longer changes in this iteration)
         mxs[(u + 1) & 1] = max_halves(lane_max(sn));
+        grows[(u + 1) & 1] = __builtin_amdgcn_ballot_w64((mxs[(u + 1) & 1] - m) * c > kTau) != 0;
         l += rs;
         schedule_iteration<2 * (DQ / 16), 4 * (DV / 32)>();
     };
