@@ -271,9 +271,18 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     flops = w.metric_flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = stored_traffic(name)
+    # Roofline of the launch: MFMA when the metric FLOPs per minimum byte
+    # exceed the ridge (peak / HBM bandwidth), else HBM (small configs).
+    min_bytes = w.min_bytes()
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / min_bytes >= ridge:
+        bound, unit, roof_peak = "mfma", "TFLOP/s", peak
+        achieved = flops / (kernel_ms * 1e-3) / 1e12
+    else:
+        bound, unit, roof_peak = "hbm", "GB/s", PEAK_HBM_GBS
+        achieved = min_bytes / (kernel_ms * 1e-3) / 1e9
 
     result = {
         "metric": "attention fwd TFLOP/s and % of MFMA peak (bf16 causal, S=16k, D=128)",
@@ -295,22 +304,24 @@ def main():
             "inputs": (f"{w.dist} Q,K sigma={w.sigma_qk:.4g}, V sigma={w.sigma_v:.4g}, "
                        f"seed {w.seed}" if w.dist == "normal" else f"{w.dist}(-1,1), seed {w.seed}"),
             "flops_per_step": flops,
-            "pct_of_mfma_peak": round(100.0 * achieved / peak, 2),
+            "pct_of_mfma_peak": round(100.0 * (flops / (kernel_ms * 1e-3) / 1e12) / peak, 2),
             # the rated peak assumes 2.4 GHz; the clock read while the same
             # step runs back to back after the timed steps gives the peak at
             # the clock the kernel actually runs at
             "sclk_mhz": sclk_mhz,
-            "pct_of_mfma_peak_at_sclk": (round(100.0 * achieved / (peak * sclk_mhz / 2400.0), 2)
-                                         if sclk_mhz else None),
+            "pct_of_mfma_peak_at_sclk": (
+                round(100.0 * (flops / (kernel_ms * 1e-3) / 1e12) / (peak * sclk_mhz / 2400.0), 2)
+                if sclk_mhz else None),
+            "min_bytes_per_step": min_bytes,
             "device": torch.cuda.get_device_name(dev),
             "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
         },
         "roofline": {
-            "bound": "mfma",
+            "bound": bound,
             "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4),
+            "peak": roof_peak,
+            "unit": unit,
+            "frac": round(achieved / roof_peak, 4),
             "traffic": traffic,
             "kernel_ms": round(kernel_ms, 4),
         },
