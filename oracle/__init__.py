@@ -49,6 +49,11 @@ def load_library(path: str) -> ctypes.CDLL:
                   ctypes.c_double, ctypes.c_int, ctypes.POINTER(i64), i64,
                   ctypes.c_int]
     f.restype = ctypes.c_int
+    g = lib.attn_ref_ext_f64
+    g.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64,
+                  ctypes.c_double, ctypes.c_int, i64, i64, i64, i64,
+                  ctypes.POINTER(i64), i64, ctypes.c_int]
+    g.restype = ctypes.c_int
     return lib
 
 
@@ -107,3 +112,62 @@ def attn_ref(q, k, v, scale: float, causal: bool, rows=None, nthreads=None,
     if rc != 0:
         raise RuntimeError(f"attn_ref_f64 failed with status {rc}")
     return (o, lse, p) if want_probs else (o, lse)
+
+
+def attn_ref_ext(q, k, v, scale: float, causal: bool, causal_offset: int = 0,
+                 window: int = 0, kv_begin: int = 0, kv_end=None, rows=None,
+                 nthreads=None, want_probs: bool = False, lib: ctypes.CDLL | None = None):
+    """``attn_ref`` with each query row i restricted to the keys j with
+    kv_begin <= j < kv_end, j <= i + causal_offset (causal) and
+    j > i + causal_offset - window (window > 0).  Rows without a visible
+    key give O = 0 and LSE = -inf."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be 4-D [B,H,S,D]")
+    B, H, S_q, D_qk = q.shape
+    if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != D_qk \
+            or v.shape[2] != k.shape[2]:
+        raise ValueError("inconsistent q/k/v shapes")
+    S_k, D_v = k.shape[2], v.shape[3]
+    if kv_end is None:
+        kv_end = S_k
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows.shape[0]
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    else:
+        n_rows, rows_p = S_q, None
+    o = np.empty((B, H, n_rows, D_v), dtype=np.float64)
+    lse = np.empty((B, H, n_rows), dtype=np.float64)
+    p = np.empty((B, H, n_rows, S_k), dtype=np.float64) if want_probs else None
+    lib = lib or _library()
+    rc = lib.attn_ref_ext_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(p),
+                              B, H, S_q, S_k, D_qk, D_v, float(scale), int(bool(causal)),
+                              int(causal_offset), int(window), int(kv_begin), int(kv_end),
+                              rows_p, n_rows, int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"attn_ref_ext_f64 failed with status {rc}")
+    return (o, lse, p) if want_probs else (o, lse)
+
+
+def merge_ref(o_parts, lse_parts):
+    """Combine partial results over disjoint key sets (fp64, plain formula):
+    LSE = ln sum_g exp(LSE_g) and O = sum_g exp(LSE_g - LSE) O_g.  A part
+    with LSE_g = -inf contributes nothing; if every part is empty the result
+    is O = 0, LSE = -inf."""
+    lse_parts = [np.asarray(x, dtype=np.float64) for x in lse_parts]
+    o_parts = [np.asarray(x, dtype=np.float64) for x in o_parts]
+    m = np.max(np.stack(lse_parts), axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    total = np.zeros_like(m_safe)
+    for lg in lse_parts:
+        total += np.where(np.isfinite(lg), np.exp(lg - m_safe), 0.0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, total, 1.0)), -np.inf)
+    o = np.zeros_like(o_parts[0])
+    for og, lg in zip(o_parts, lse_parts):
+        wgt = np.where(np.isfinite(lg) & finite, np.exp(lg - np.where(finite, lse, 0.0)), 0.0)
+        o += wgt[..., None] * og
+    return o, lse

@@ -34,6 +34,20 @@
  *   - masked keys are simply left out of every sum (exact);
  *   - LSE uses the natural logarithm of the scaled scores.
  *
+ * The extended entry point (attn_ref_ext_f64) restricts each row to one
+ * contiguous key range, which covers the page-2 variants:
+ *   - a key range [kv_begin, kv_end): one chunk of a split key sequence
+ *     (the continuation case of attention_fwd_triton3, whose partial
+ *     results merge into the full one);
+ *   - a signed causal offset: key j visible iff j <= i + causal_offset
+ *     (attention_llama's start_position shifts the diagonal; S_k - S_q
+ *     aligns it to the bottom-right corner);
+ *   - a window W > 0: only keys j > i + causal_offset - W (the sliding
+ *     window of attention_fwd_triton3 case 1, read as the W keys ending at
+ *     the diagonal).
+ *   A row that sees no key gets O = 0 and LSE = -infinity (the neutral
+ *   element of the merge).
+ *
  * Layout: contiguous row-major Q[B,H,S_q,D_qk], K[B,H,S_k,D_qk],
  * V[B,H,S_k,D_v], O[B,H,S_q,D_v], LSE[B,H,S_q] (all double).
  * With a row list, only those query rows are computed and O / LSE are
@@ -50,6 +64,7 @@ typedef struct {
     int64_t B, H, S_q, S_k, D_qk, D_v;
     double scale;
     int causal;
+    int64_t coff, window, kv_begin, kv_end;   /* key range of every row, see above */
     const int64_t *rows;
     int64_t n_rows;          /* rows computed per slice */
     int64_t first, last;     /* work items [first, last) over slices*n_rows */
@@ -64,13 +79,31 @@ static void oracle_row(const oracle_job *jb, int64_t slice, int64_t out_row,
     const double *k = jb->K + slice * jb->S_k * jb->D_qk;
     const double *v = jb->V + slice * jb->S_k * jb->D_v;
 
-    /* valid keys: all of them, or j <= i when causal */
-    int64_t n_valid = jb->S_k;
-    if (jb->causal && i + 1 < n_valid)
-        n_valid = i + 1;
+    /* visible keys j in [lo, hi): the key range, then j <= i + coff when
+       causal, then j > i + coff - window when windowed */
+    int64_t lo = jb->kv_begin, hi = jb->kv_end;
+    if (jb->causal && i + jb->coff + 1 < hi)
+        hi = i + jb->coff + 1;
+    if (jb->window > 0 && i + jb->coff - jb->window + 1 > lo)
+        lo = i + jb->coff - jb->window + 1;
+
+    double *o = jb->O + (slice * jb->n_rows + out_row) * jb->D_v;
+    if (hi <= lo) {
+        /* no visible key: the merge's neutral element */
+        for (int64_t e = 0; e < jb->D_v; ++e)
+            o[e] = 0.0;
+        if (jb->LSE)
+            jb->LSE[slice * jb->n_rows + out_row] = -INFINITY;
+        if (jb->P) {
+            double *p = jb->P + (slice * jb->n_rows + out_row) * jb->S_k;
+            for (int64_t j = 0; j < jb->S_k; ++j)
+                p[j] = 0.0;
+        }
+        return;
+    }
 
     /* 1. score_dot, then the scale */
-    for (int64_t j = 0; j < n_valid; ++j) {
+    for (int64_t j = lo; j < hi; ++j) {
         double dot = 0.0;
         for (int64_t d = 0; d < jb->D_qk; ++d)
             dot += q[d] * k[j * jb->D_qk + d];
@@ -78,23 +111,22 @@ static void oracle_row(const oracle_job *jb, int64_t slice, int64_t out_row,
     }
     /* 2. score_max, seeded with -infinity */
     double m = -INFINITY;
-    for (int64_t j = 0; j < n_valid; ++j)
+    for (int64_t j = lo; j < hi; ++j)
         if (s[j] > m)
             m = s[j];
     /* 3. score_exp_sum: the shifted exponentials summed */
     double l = 0.0;
-    for (int64_t j = 0; j < n_valid; ++j)
+    for (int64_t j = lo; j < hi; ++j)
         l += exp(s[j] - m);
     /* 4. weighted_sum: weight = exp(s_j - m) / l, then weight * V[j, e] */
-    for (int64_t j = 0; j < n_valid; ++j)
+    for (int64_t j = lo; j < hi; ++j)
         w[j] = exp(s[j] - m) / l;
     for (int64_t e = 0; e < jb->D_v; ++e)
         acc[e] = 0.0;
-    for (int64_t j = 0; j < n_valid; ++j)
+    for (int64_t j = lo; j < hi; ++j)
         for (int64_t e = 0; e < jb->D_v; ++e)
             acc[e] += w[j] * v[j * jb->D_v + e];
 
-    double *o = jb->O + (slice * jb->n_rows + out_row) * jb->D_v;
     for (int64_t e = 0; e < jb->D_v; ++e)
         o[e] = acc[e];
     if (jb->LSE)
@@ -102,7 +134,7 @@ static void oracle_row(const oracle_job *jb, int64_t slice, int64_t out_row,
     if (jb->P) {
         double *p = jb->P + (slice * jb->n_rows + out_row) * jb->S_k;
         for (int64_t j = 0; j < jb->S_k; ++j)
-            p[j] = j < n_valid ? w[j] : 0.0;
+            p[j] = (j >= lo && j < hi) ? w[j] : 0.0;
     }
 }
 
@@ -129,21 +161,29 @@ static void *oracle_worker(void *arg)
 }
 
 /*
+ * attn_ref_ext_f64: the definition above with each row's keys restricted to
+ * [max(kv_begin, i + causal_offset - window + 1) (window > 0 only),
+ *  min(kv_end, i + causal_offset + 1) (causal only)).
+ * Requires 0 <= kv_begin <= kv_end <= S_k and window >= 0.
+ *
  * Returns 0 on success, 1 for a bad argument (null pointer, a dimension
- * below 1, a row index outside [0, S_q)), 2 if a thread could not be
- * started, 3 if a work buffer could not be allocated.
- * P, when not NULL, receives the softmax weights [B,H,rows,S_k] (0 where a
- * key is masked); LSE may be NULL.
+ * below 1, a row index outside [0, S_q), a key range outside [0, S_k]),
+ * 2 if a thread could not be started, 3 if a work buffer could not be
+ * allocated.  P, when not NULL, receives the softmax weights
+ * [B,H,rows,S_k] (0 where a key is masked); LSE may be NULL.
  */
-int attn_ref_f64(const double *Q, const double *K, const double *V,
-                 double *O, double *LSE, double *P,
-                 int64_t B, int64_t H, int64_t S_q, int64_t S_k,
-                 int64_t D_qk, int64_t D_v, double scale, int causal,
-                 const int64_t *rows, int64_t n_rows, int nthreads)
+int attn_ref_ext_f64(const double *Q, const double *K, const double *V,
+                     double *O, double *LSE, double *P,
+                     int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                     int64_t D_qk, int64_t D_v, double scale, int causal,
+                     int64_t causal_offset, int64_t window, int64_t kv_begin,
+                     int64_t kv_end, const int64_t *rows, int64_t n_rows, int nthreads)
 {
     if (!Q || !K || !V || !O)
         return 1;
     if (B < 1 || H < 1 || S_q < 1 || S_k < 1 || D_qk < 1 || D_v < 1)
+        return 1;
+    if (kv_begin < 0 || kv_end < kv_begin || kv_end > S_k || window < 0)
         return 1;
     if (rows) {
         if (n_rows < 1)
@@ -175,6 +215,8 @@ int attn_ref_f64(const double *Q, const double *K, const double *V,
         jb->B = B; jb->H = H; jb->S_q = S_q; jb->S_k = S_k;
         jb->D_qk = D_qk; jb->D_v = D_v;
         jb->scale = scale; jb->causal = causal;
+        jb->coff = causal_offset; jb->window = window;
+        jb->kv_begin = kv_begin; jb->kv_end = kv_end;
         jb->rows = rows; jb->n_rows = n_rows;
         jb->first = total * t / nthreads;
         jb->last = total * (t + 1) / nthreads;
@@ -197,4 +239,15 @@ int attn_ref_f64(const double *Q, const double *K, const double *V,
     free(jobs);
     free(tids);
     return rc;
+}
+
+/* The plain definition over every key (top-left causal when `causal`). */
+int attn_ref_f64(const double *Q, const double *K, const double *V,
+                 double *O, double *LSE, double *P,
+                 int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                 int64_t D_qk, int64_t D_v, double scale, int causal,
+                 const int64_t *rows, int64_t n_rows, int nthreads)
+{
+    return attn_ref_ext_f64(Q, K, V, O, LSE, P, B, H, S_q, S_k, D_qk, D_v, scale, causal,
+                            0, 0, 0, S_k, rows, n_rows, nthreads);
 }

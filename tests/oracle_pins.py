@@ -12,7 +12,11 @@ what the pages and the mathematics fix:
   (logistic weights), a dominant key, scores far from zero;
 * invariants: weights sum to one, key permutation, score shift, linearity in
   V, causal prefix, zero padding of the head dims, row sampling, threads;
-* the worked example printed on tiny.accy.kernel.library.attention.
+* the worked example printed on tiny.accy.kernel.library.attention;
+* for the extended entry point (key range, signed causal offset, window):
+  torch's fp64 attention on the truncated key prefix, the 40-digit brute
+  force on explicit key sets, a one-key window, rows without keys, and the
+  merge of partial results over a key partition.
 """
 from __future__ import annotations
 
@@ -340,6 +344,120 @@ def pin_page_worked_example(lib):
     assert err <= g["abs_tolerance_f32"], f"page example vs page's f32 order: {err}"
 
 
+# ------------------------------------ extended oracle: key ranges, offsets, windows
+def _ext(lib, q, k, v, scale, causal, **kw):
+    return oracle.attn_ref_ext(q, k, v, scale, causal, lib=lib, nthreads=2, **kw)
+
+
+def _visible(i, S_k, causal, coff, window, kv_begin, kv_end):
+    """The keys row i sees, listed one by one (the definition, no ranges)."""
+    keys = []
+    for j in range(S_k):
+        ok = kv_begin <= j < kv_end
+        if causal:
+            ok = ok and j <= i + coff
+        if window > 0:
+            ok = ok and j > i + coff - window
+        if ok:
+            keys.append(j)
+    return keys
+
+
+def pin_ext_bottom_right_library(lib):
+    """Offset S_k - S_q (bottom-right alignment): row i is plain attention
+    over the key prefix 0 .. i + S_k - S_q, computed by the library routine
+    on that prefix."""
+    rng = np.random.default_rng(31)
+    for S_q, S_k, D in ((5, 9, 4), (7, 7, 3), (3, 12, 8), (16, 40, 16)):
+        q = _randn(rng, 1, 2, S_q, D)
+        k = _randn(rng, 1, 2, S_k, D)
+        v = _randn(rng, 1, 2, S_k, D + 1)
+        scale = 0.6
+        o, lse = _ext(lib, q, k, v, scale, True, causal_offset=S_k - S_q)
+        for i in range(S_q):
+            n = i + S_k - S_q + 1
+            o_t, lse_t = _library_sdpa(q[:, :, i:i + 1], k[:, :, :n], v[:, :, :n], scale, False)
+            _close(o[:, :, i], o_t[:, :, 0], 1e-12, f"bottom-right {S_q}x{S_k} row {i} O")
+            _close(lse[:, :, i], lse_t[:, :, 0], 1e-12, f"bottom-right {S_q}x{S_k} row {i} LSE")
+
+
+def pin_ext_brute_force(lib):
+    """40-digit brute force over the explicitly listed visible keys, for key
+    ranges, signed offsets and windows; rows without keys: O = 0, LSE = -inf."""
+    rng = np.random.default_rng(32)
+    for trial in range(60):
+        S_q, S_k = int(rng.integers(1, 7)), int(rng.integers(1, 9))
+        D_qk, D_v = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+        causal = bool(rng.integers(0, 2))
+        coff = int(rng.integers(-3, 5))
+        window = int(rng.integers(0, 4))
+        kv_begin = int(rng.integers(0, S_k + 1))
+        kv_end = int(rng.integers(kv_begin, S_k + 1))
+        scale = float(rng.uniform(-1.2, 1.2))
+        q = _randn(rng, 1, 1, S_q, D_qk, sigma=1.5)
+        k = _randn(rng, 1, 1, S_k, D_qk, sigma=1.5)
+        v = _randn(rng, 1, 1, S_k, D_v)
+        o, lse = _ext(lib, q, k, v, scale, causal, causal_offset=coff, window=window,
+                      kv_begin=kv_begin, kv_end=kv_end)
+        for i in range(S_q):
+            keys = _visible(i, S_k, causal, coff, window, kv_begin, kv_end)
+            tag = (f"ext trial {trial} row {i} ({S_q}x{S_k} c{causal} off{coff} w{window} "
+                   f"[{kv_begin},{kv_end}))")
+            if not keys:
+                assert np.all(o[0, 0, i] == 0.0), tag + ": O of an empty row"
+                assert lse[0, 0, i] == -np.inf, tag + ": LSE of an empty row"
+                continue
+            o_mp, lse_mp = _mp_attention_row(q[0, 0, i], k[0, 0][keys], v[0, 0][keys], scale,
+                                             len(keys))
+            _close(o[0, 0, i], o_mp, 1e-13, tag + " O")
+            _close(lse[0, 0, i], lse_mp, 1e-13, tag + " LSE")
+
+
+def pin_ext_window_of_one(lib):
+    """Causal window of one key: row i sees only key i + offset, so O = V
+    there and LSE = its scaled score."""
+    rng = np.random.default_rng(33)
+    S_q, S_k, D = 9, 12, 5
+    q = _randn(rng, 1, 1, S_q, D)
+    k = _randn(rng, 1, 1, S_k, D)
+    v = _randn(rng, 1, 1, S_k, D)
+    for coff in (0, 2, -1):
+        o, lse = _ext(lib, q, k, v, 0.7, True, causal_offset=coff, window=1)
+        for i in range(S_q):
+            j = i + coff
+            if 0 <= j < S_k:
+                _close(o[0, 0, i], v[0, 0, j], 1e-15, f"window 1 off {coff} row {i}")
+                _close(lse[0, 0, i], 0.7 * float(q[0, 0, i] @ k[0, 0, j]), 1e-14,
+                       f"window 1 off {coff} row {i} LSE")
+            else:
+                assert lse[0, 0, i] == -np.inf and np.all(o[0, 0, i] == 0.0)
+
+
+def pin_ext_partition_merge(lib):
+    """Split the keys into consecutive chunks: the merge of the chunks'
+    (O, LSE) is the result over all keys, for causal (with offsets) and
+    non-causal rows, including chunks some rows see nothing of."""
+    rng = np.random.default_rng(34)
+    for trial in range(20):
+        S_q, S_k = int(rng.integers(1, 30)), int(rng.integers(2, 60))
+        causal = bool(rng.integers(0, 2))
+        coff = int(rng.integers(-4, 8)) if causal else 0
+        q = _randn(rng, 1, 2, S_q, 6)
+        k = _randn(rng, 1, 2, S_k, 6)
+        v = _randn(rng, 1, 2, S_k, 3)
+        cuts = sorted(set(int(x) for x in rng.integers(1, S_k, size=int(rng.integers(1, 5)))))
+        bounds = [0] + cuts + [S_k]
+        parts = [_ext(lib, q, k, v, 0.45, causal, causal_offset=coff, kv_begin=a, kv_end=b)
+                 for a, b in zip(bounds, bounds[1:])]
+        o_m, lse_m = oracle.merge_ref([p[0] for p in parts], [p[1] for p in parts])
+        o_f, lse_f = _ext(lib, q, k, v, 0.45, causal, causal_offset=coff)
+        empty = ~np.isfinite(lse_f)
+        assert np.array_equal(empty, ~np.isfinite(lse_m)), f"merge trial {trial}: empty rows"
+        _close(o_m[~empty], o_f[~empty], 1e-12, f"merge trial {trial} O")
+        _close(lse_m[~empty], lse_f[~empty], 1e-12, f"merge trial {trial} LSE")
+        assert np.all(o_m[empty] == 0.0)
+
+
 PINS = [
     pin_library_sdpa,
     pin_highprec_unshifted,
@@ -356,4 +474,8 @@ PINS = [
     pin_head_dim_padding,
     pin_rows_and_threads,
     pin_page_worked_example,
+    pin_ext_bottom_right_library,
+    pin_ext_brute_force,
+    pin_ext_window_of_one,
+    pin_ext_partition_merge,
 ]

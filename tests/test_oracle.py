@@ -23,7 +23,7 @@ def test_oracle_pin(pin, oracle_lib):
 # (what the mistake is, text in attn_ref.c, replacement)
 MUTATIONS = [
     ("scale dropped", "s[j] = jb->scale * dot;", "s[j] = dot;"),
-    ("causal excludes the diagonal", "n_valid = i + 1;", "n_valid = i;"),
+    ("causal excludes the diagonal", "hi = i + jb->coff + 1;", "hi = i + jb->coff;"),
     ("wrong sign of the max shift", "l += exp(s[j] - m);", "l += exp(s[j] + m);"),
     ("V read transposed", "acc[e] += w[j] * v[j * jb->D_v + e];",
      "acc[e] += w[j] * v[e * jb->S_k + j];"),
@@ -38,8 +38,16 @@ MUTATIONS = [
      "(slice * jb->S_q + (i > 0 ? i - 1 : 0)) * jb->D_qk"),
     ("V slice stride uses D_qk", "jb->V + slice * jb->S_k * jb->D_v",
      "jb->V + slice * jb->S_k * jb->D_qk"),
-    ("first key skipped", "for (int64_t j = 0; j < n_valid; ++j)\n        w[j]",
-     "for (int64_t j = 1; j < n_valid; ++j)\n        w[j]"),
+    ("first key skipped", "for (int64_t j = lo; j < hi; ++j)\n        w[j]",
+     "for (int64_t j = lo + 1; j < hi; ++j)\n        w[j]"),
+    ("causal offset ignored", "hi = i + jb->coff + 1;", "hi = i + 1;"),
+    ("window one key too wide", "lo = i + jb->coff - jb->window + 1;",
+     "lo = i + jb->coff - jb->window;"),
+    ("key range end inclusive", "int64_t lo = jb->kv_begin, hi = jb->kv_end;",
+     "int64_t lo = jb->kv_begin, hi = jb->kv_end < jb->S_k ? jb->kv_end + 1 : jb->kv_end;"),
+    ("key range start ignored", "int64_t lo = jb->kv_begin, hi", "int64_t lo = 0, hi"),
+    ("empty row LSE zero", "jb->LSE[slice * jb->n_rows + out_row] = -INFINITY;",
+     "jb->LSE[slice * jb->n_rows + out_row] = 0.0;"),
 ]
 
 
