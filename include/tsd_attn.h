@@ -116,6 +116,125 @@ int attn_fwd_plan_block(const tsd_plan *plan, int64_t S_q, int64_t S_k,
                         int64_t block, int64_t *q_block, int64_t *slice,
                         int64_t *kv_steps);
 
+/*
+ * ------------------------------------------------------------------------
+ * Extended visibility, key chunks and the merge of partial results.
+ *
+ * These entry points run on the LDS-direct kernel only: dtype TSD_F16 or
+ * TSD_BF16, Q/K/V (and a 16-bit O) 16-byte aligned, D_qk and D_v multiples
+ * of 8 (else TSD_ERR_UNSUPPORTED).  Buffer ownership, threading and
+ * synchronisation are as for attn_fwd.
+ *
+ * Key visibility (tsd_mask).  Query row i of a slice sees exactly the keys
+ *   j in [lo_i, hi_i),
+ *   lo_i = max(kv_begin, i + causal_offset - window + 1)   (window > 0)
+ *        = kv_begin                                          (window = 0)
+ *   hi_i = min(kv_end, i + causal_offset + 1)                (causal)
+ *        = kv_end                                            (not causal)
+ * and the row's result is the definition above restricted to those keys.
+ * A row that sees no key gets O = 0 and LSE = -infinity, the neutral
+ * element of the merge below.  NULL means {0, 0, 0, S_k}: attn_fwd's own
+ * visibility.
+ *   - causal_offset moves the diagonal: S_k - S_q aligns it to the bottom
+ *     right (VeriTile proof coverage, attention_llama: the causal case
+ *     whose start_position shifts the key limit of every query block).
+ *   - window keeps the `window` keys ending at the diagonal (VeriTile proof
+ *     coverage, attention_fwd_triton3 case 1, the sliding-window keep
+ *     predicate; its complement, the keys before the window, is the
+ *     causal mask with causal_offset - window and no window).
+ *   - [kv_begin, kv_end) restricts the keys (one chunk of a split key
+ *     sequence: attention_fwd_triton3 case 4, the continuation that merges
+ *     a chunk's result into the running one).
+ * Invalid: kv_begin < 0, kv_end > S_k, kv_begin > kv_end, window < 0
+ * (TSD_ERR_SHAPE); |causal_offset| or window above 2^30
+ * (TSD_ERR_UNSUPPORTED).
+ */
+typedef struct tsd_mask {
+    int64_t causal_offset;  /* causal: key j visible to row i iff j <= i + causal_offset */
+    int64_t window;         /* > 0: also j > i + causal_offset - window; 0: no window  */
+    int64_t kv_begin;       /* first key of the range                                   */
+    int64_t kv_end;         /* one past the last key of the range                       */
+} tsd_mask;
+
+/*
+ * attn_fwd_ext — attn_fwd with the visibility of `mask`.  O [B,H,S_q,D_v]
+ * of `dtype`, LSE [B,H,S_q] f32 (may be NULL).  Same statuses as attn_fwd,
+ * plus the mask and fast-path conditions above.
+ */
+int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                 int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                 int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+                 const tsd_mask *mask, void *stream);
+
+/*
+ * attn_fwd_partial — one partial result per key chunk (VeriTile proof
+ * coverage, attention_fwd_triton3 case 3: a pass that writes O and a per-row
+ * statistic for a later continuation).  Chunk s (0 <= s < n_splits) covers
+ * the keys [kv_begin + s*split_len, kv_begin + (s+1)*split_len), cut to
+ * [kv_begin, kv_end) and to each row's visibility; it writes
+ *   O_parts   [n_splits,B,H,S_q,D_v] f32 (16-byte aligned): softmax over
+ *             the chunk's visible keys times V (0 if none);
+ *   LSE_parts [n_splits,B,H,S_q] f32 (required): ln of the chunk's sum of
+ *             exp of the scaled scores (-infinity if none).
+ * split_len >= 1; a multiple of 64 keeps chunks on whole key tiles.
+ * Merging the n_splits results with attn_merge gives attn_fwd_ext's result
+ * up to rounding.
+ */
+int attn_fwd_partial(const void *Q, const void *K, const void *V,
+                     float *O_parts, float *LSE_parts,
+                     int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                     int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+                     const tsd_mask *mask, int64_t n_splits, int64_t split_len,
+                     void *stream);
+
+/*
+ * attn_merge — combine n_parts partial results of the same rows (VeriTile
+ * proof coverage, attention_fwd_triton3 case 4, the continuation pass: the
+ * running output is rescaled by the change of the row statistic and the
+ * new chunk added).  For every row r:
+ *   LSE[r] = ln sum_g exp(LSE_parts[g,r])
+ *   O[r,:] = sum_g exp(LSE_parts[g,r] - LSE[r]) * O_parts[g,r,:]
+ * (O = 0, LSE = -infinity when every part is -infinity).  O_parts
+ * [n_parts,B,H,S_q,D_v] and LSE_parts [n_parts,B,H,S_q] are f32 (4-byte
+ * aligned); O [B,H,S_q,D_v] of `dtype` (any of the three, element aligned);
+ * LSE [B,H,S_q] f32 or NULL.  Any D_v in 1..128.  Outputs must not overlap
+ * the parts (TSD_ERR_ALIAS).
+ */
+int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
+               int64_t B, int64_t H, int64_t S_q, int64_t D_v,
+               void *O, float *LSE, int dtype, void *stream);
+
+/*
+ * attn_splitkv_plan — the chunking attn_fwd_splitkv uses (host only).
+ * n_splits <= 0 lets the library choose: enough chunks that the launch
+ * covers the 256 compute units about twice, chunks of at least 512 keys,
+ * at most 256 chunks.  Reports the chunk count actually used (chunks are
+ * whole 64-key tiles, so it may come out below the request), the chunk
+ * length in keys and the workspace bytes attn_fwd_splitkv needs (0 when a
+ * single chunk is used: then no workspace is touched).
+ */
+int attn_splitkv_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                      int64_t D_qk, int64_t D_v, int causal, int dtype,
+                      const tsd_mask *mask, int64_t n_splits,
+                      int64_t *splits_out, int64_t *split_len_out,
+                      int64_t *workspace_bytes);
+
+/*
+ * attn_fwd_splitkv — attn_fwd_ext computed as attn_fwd_partial over key
+ * chunks followed by attn_merge, both enqueued on `stream`.  For launches
+ * with few query blocks and many keys (long-context decoding, chunked
+ * prefill) the chunks fill the chip that one workgroup per query block
+ * cannot.  `workspace` (256-byte aligned, at least the planned bytes,
+ * caller-owned, disjoint from every other buffer) holds the partial
+ * results between the two launches; it may be NULL when the plan needs
+ * none.  Too small a workspace: TSD_ERR_SHAPE.
+ */
+int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                     int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                     int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+                     const tsd_mask *mask, int64_t n_splits,
+                     void *workspace, int64_t workspace_bytes, void *stream);
+
 /* attn_status_string — static text for a status code (never NULL). */
 const char *attn_status_string(int status);
 

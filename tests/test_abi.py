@@ -217,3 +217,104 @@ def test_product_code_does_not_touch_the_oracle():
                 assert "liboracle" not in text and "attn_ref" not in text, f
     hdr = open(HEADER).read()
     assert "oracle" not in hdr.lower()
+
+
+# ------------------------------------------------ extended entry points
+# Every call below is rejected on the host before any HIP call.
+MK = tsd.make_mask
+
+
+def ext(q=QA, k=KA, v=VA, o=OA, lse=LA, dtype=2, mask=None, **dims):
+    d = dict(GOOD)
+    d.update(dims)
+    return tsd.attn_fwd_ext_raw(q, k, v, o, lse, d["B"], d["H"], d["S_q"], d["S_k"],
+                                d["D_qk"], d["D_v"], 0.125, 1, dtype, mask)
+
+
+def part(op=OA, lp=LA, n=2, ln=64, mask=None, dtype=2, q=QA, **dims):
+    d = dict(GOOD)
+    d.update(dims)
+    return tsd.attn_fwd_partial_raw(q, KA, VA, op, lp, d["B"], d["H"], d["S_q"], d["S_k"],
+                                    d["D_qk"], d["D_v"], 0.125, 0, dtype, mask, n, ln)
+
+
+@pytest.mark.parametrize("mask,status", [
+    (MK(128, kv_begin=-1), 2), (MK(128, kv_end=129), 2), (MK(128, kv_begin=50, kv_end=49), 2),
+    (MK(128, window=-1), 2), (MK(128, causal_offset=(1 << 30) + 1), 3),
+    (MK(128, causal_offset=-(1 << 30) - 1), 3), (MK(128, window=(1 << 30) + 1), 3),
+])
+def test_ext_bad_mask(lib, mask, status):
+    assert ext(mask=mask) == status
+    assert part(mask=mask) == status
+
+
+def test_ext_fast_path_only(lib):
+    assert ext(dtype=0) == 3                  # f32 inputs
+    assert ext(D_qk=60, D_v=60) == 3          # widths not a multiple of 8
+    assert ext(q=QA + 8) == 3                 # not 16-byte aligned
+    assert ext(o=OA + 8) == 3
+    assert part(dtype=0) == 3
+    assert part(op=OA + 4) == 3               # f32 partial O not 16-byte aligned
+    assert ext(o=None) == 1 and ext(q=None) == 1
+    assert part(op=None) == 1 and part(lp=None) == 1
+    assert ext(S_k=0) == 2
+
+
+def test_ext_alias(lib):
+    assert ext(o=KA) == 5
+    assert ext(lse=OA + 64) == 5
+    assert part(op=QA) == 5
+    assert part(lp=VA + 16) == 5
+    # the chunked output spans n times the slice outputs: chunk 1 would reach LA
+    o_bytes = 1 * 2 * 128 * 64 * 4
+    assert part(op=LA - o_bytes, n=2) == 5
+
+
+def test_partial_bad_chunks(lib):
+    assert part(n=0) == 2 and part(ln=0) == 2
+    assert part(n=1 << 20, ln=1 << 12) == 3   # chunk bounds beyond int32
+
+
+def merge(op=OA, lp=LA, n=3, o=VA, lse=KA, dtype=2, B=1, H=2, S_q=128, D_v=64):
+    return tsd.attn_merge_raw(op, lp, n, B, H, S_q, D_v, o, lse, dtype)
+
+
+def test_merge_rejects(lib):
+    assert merge(op=None) == 1 and merge(lp=None) == 1 and merge(o=None) == 1
+    assert merge(n=0) == 2 and merge(D_v=0) == 2 and merge(S_q=0) == 2
+    assert merge(D_v=129) == 3 and merge(dtype=5) == 3
+    assert merge(op=OA + 2) == 3 and merge(o=VA + 1) == 3
+    assert merge(o=OA + 4096) == 5            # output inside the partial O
+    assert merge(lse=LA) == 5                 # LSE on the partial LSE
+    assert merge(lse=VA + 8) == 5             # LSE inside O
+
+
+def test_splitkv_plan(lib):
+    # few query blocks, many keys: chunks until the grid covers the chip twice
+    n, ln, ws = tsd.attn_splitkv_plan(1, 8, 512, 131072, 128, 128, False, "bf16")
+    plan = tsd.attn_fwd_plan(1, 8, 512, 131072, 128, 128, False, "bf16")
+    assert plan.grid * n >= 512 and ln % 64 == 0 and n * ln >= 131072
+    assert ws == math.ceil(n * 8 * 512 * 128 * 4 / 256) * 256 + math.ceil(n * 8 * 512 * 4 / 256) * 256
+    # a full grid keeps one chunk and needs no workspace
+    assert tsd.attn_splitkv_plan(4, 16, 4096, 4096, 128, 128, True, "bf16") == (1, 4096, 0)
+    # requested counts: chunks are whole tiles and none lies past the range
+    n, ln, _ = tsd.attn_splitkv_plan(1, 1, 64, 1000, 64, 64, False, "bf16", None, 7)
+    assert ln == 192 and n == 6
+    n, ln, _ = tsd.attn_splitkv_plan(1, 1, 64, 1000, 64, 64, False, "bf16",
+                                     MK(1000, kv_begin=100, kv_end=300), 4)
+    assert (n, ln) == (4, 64)
+    with pytest.raises(tsd.TsdError):
+        tsd.attn_splitkv_plan(1, 1, 64, 1000, 64, 64, False, "f32")
+    with pytest.raises(tsd.TsdError):
+        tsd.attn_splitkv_plan(1, 1, 64, 1000, 64, 64, False, "bf16", None, 300)
+
+
+def test_splitkv_workspace_checks(lib):
+    n, ln, ws = tsd.attn_splitkv_plan(1, 2, 128, 4096, 64, 64, False, "bf16", None, 4)
+    assert n == 4 and ws > 0
+    args = (QA, KA, VA, OA, LA, 1, 2, 128, 4096, 64, 64, 0.125, 0, 2, None, 4)
+    assert tsd.attn_fwd_splitkv_raw(*args, None, ws) == 1          # no workspace
+    assert tsd.attn_fwd_splitkv_raw(*args, 0x60000000, ws - 1) == 2  # too small
+    assert tsd.attn_fwd_splitkv_raw(*args, 0x60000000 + 64, ws) == 3  # not 256-aligned
+    assert tsd.attn_fwd_splitkv_raw(*args, OA, ws) == 5             # workspace on O
+    assert tsd.attn_fwd_splitkv_raw(*args, KA - 256, ws) == 5       # workspace into K

@@ -12,7 +12,9 @@ import math
 import os
 
 __all__ = ["attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string",
-           "TsdError", "library", "LIBRARY_PATH", "DTYPE_CODES", "STATUS"]
+           "attn_fwd_ext", "attn_fwd_partial", "attn_merge", "attn_splitkv_plan",
+           "attn_fwd_splitkv", "TsdMask", "TsdError", "library", "LIBRARY_PATH",
+           "DTYPE_CODES", "STATUS"]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsd_attn.so")
 
@@ -27,7 +29,9 @@ STATUS = {
 }
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 
-EXPORTED = ("attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string")
+EXPORTED = ("attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string",
+            "attn_fwd_ext", "attn_fwd_partial", "attn_merge", "attn_splitkv_plan",
+            "attn_fwd_splitkv")
 
 
 class TsdError(RuntimeError):
@@ -60,6 +64,23 @@ class TsdPlan(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class TsdMask(ctypes.Structure):
+    """Key visibility of the extended entry points: row i sees keys
+    [max(kv_begin, i + causal_offset - window + 1) if window else kv_begin,
+     min(kv_end, i + causal_offset + 1) if causal else kv_end)."""
+    _fields_ = [
+        ("causal_offset", ctypes.c_int64),
+        ("window", ctypes.c_int64),
+        ("kv_begin", ctypes.c_int64),
+        ("kv_end", ctypes.c_int64),
+    ]
+
+
+def make_mask(S_k, causal_offset=0, window=0, kv_begin=0, kv_end=None) -> TsdMask:
+    return TsdMask(int(causal_offset), int(window), int(kv_begin),
+                   int(S_k if kv_end is None else kv_end))
+
+
 _lib = None
 
 
@@ -85,6 +106,22 @@ def library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.attn_fwd_plan_block.restype = ctypes.c_int
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
+    mp, f, ci = ctypes.POINTER(TsdMask), ctypes.c_float, ctypes.c_int
+    lib.attn_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f, ci, ci,
+                                 mp, vp]
+    lib.attn_fwd_ext.restype = ci
+    lib.attn_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f, ci,
+                                     ci, mp, i64, i64, vp]
+    lib.attn_fwd_partial.restype = ci
+    lib.attn_merge.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, ci, vp]
+    lib.attn_merge.restype = ci
+    lib.attn_splitkv_plan.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, mp, i64,
+                                      ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                      ctypes.POINTER(i64)]
+    lib.attn_splitkv_plan.restype = ci
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f, ci,
+                                     ci, mp, i64, vp, i64, vp]
+    lib.attn_fwd_splitkv.restype = ci
     _lib = lib
     return lib
 
@@ -120,6 +157,179 @@ def attn_fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk, D_v,
     code = DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
     return library().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk, D_v,
                               float(scale), int(bool(causal)), code, stream)
+
+
+def _code(dtype) -> int:
+    return DTYPE_CODES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _mask_ref(mask):
+    return None if mask is None else ctypes.byref(mask)
+
+
+def attn_fwd_ext_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk, D_v, scale,
+                     causal, dtype, mask=None, stream=None) -> int:
+    return library().attn_fwd_ext(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk,
+                                  D_v, float(scale), int(bool(causal)), _code(dtype),
+                                  _mask_ref(mask), stream)
+
+
+def attn_fwd_partial_raw(q_ptr, k_ptr, v_ptr, op_ptr, lp_ptr, B, H, S_q, S_k, D_qk, D_v,
+                         scale, causal, dtype, mask, n_splits, split_len, stream=None) -> int:
+    return library().attn_fwd_partial(q_ptr, k_ptr, v_ptr, op_ptr, lp_ptr, B, H, S_q, S_k,
+                                      D_qk, D_v, float(scale), int(bool(causal)), _code(dtype),
+                                      _mask_ref(mask), n_splits, split_len, stream)
+
+
+def attn_merge_raw(op_ptr, lp_ptr, n_parts, B, H, S_q, D_v, o_ptr, lse_ptr, dtype,
+                   stream=None) -> int:
+    return library().attn_merge(op_ptr, lp_ptr, n_parts, B, H, S_q, D_v, o_ptr, lse_ptr,
+                                _code(dtype), stream)
+
+
+def attn_fwd_splitkv_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk, D_v,
+                         scale, causal, dtype, mask, n_splits, ws_ptr, ws_bytes,
+                         stream=None) -> int:
+    return library().attn_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k,
+                                      D_qk, D_v, float(scale), int(bool(causal)), _code(dtype),
+                                      _mask_ref(mask), n_splits, ws_ptr, ws_bytes, stream)
+
+
+def attn_splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal=False, dtype="bf16", mask=None,
+                      n_splits=0):
+    """(chunks, keys per chunk, workspace bytes) attn_fwd_splitkv would use."""
+    n, ln, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(library().attn_splitkv_plan(B, H, S_q, S_k, D_qk, D_v, int(bool(causal)),
+                                       _code(dtype), _mask_ref(mask), n_splits,
+                                       ctypes.byref(n), ctypes.byref(ln), ctypes.byref(ws)))
+    return n.value, ln.value, ws.value
+
+
+def _qkv(q, k, v):
+    """Validate q, k, v tensors; returns (dtype code, B, H, S_q, S_k, D_qk, D_v)."""
+    import torch
+
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if q.dtype not in codes or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype among float32, float16, bfloat16")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B,H,S,D]")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, H, S_q, D_qk = q.shape
+    S_k, D_v = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, H, S_k, D_qk) or tuple(v.shape) != (B, H, S_k, D_v):
+        raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} "
+                         f"v{tuple(v.shape)}")
+    return codes[q.dtype], B, H, S_q, S_k, D_qk, D_v
+
+
+def _buffer(t, shape, dtype, like, name):
+    import torch
+
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous()
+            or t.device != like.device):
+        raise ValueError(f"{name} must be a contiguous {dtype} {list(shape)} tensor on "
+                         f"{like.device}")
+    return t
+
+
+def _stream(stream, device):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def attn_fwd_ext(q, k, v, scale=None, causal=False, causal_offset=0, window=0, kv_begin=0,
+                 kv_end=None, out=None, lse=None, stream=None):
+    """attn_fwd restricted per row to the keys of the mask (see TsdMask);
+    rows that see no key get O = 0 and LSE = -inf.  16-bit inputs only."""
+    import torch
+
+    code, B, H, S_q, S_k, D_qk, D_v = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_qk)
+    out = _buffer(out, (B, H, S_q, D_v), q.dtype, q, "out")
+    lse = _buffer(lse, (B, H, S_q), torch.float32, q, "lse")
+    mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
+    _check(attn_fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal, code,
+                            mask, _stream(stream, q.device)))
+    return out, lse
+
+
+def attn_fwd_partial(q, k, v, n_splits, split_len, scale=None, causal=False, causal_offset=0,
+                     window=0, kv_begin=0, kv_end=None, o_parts=None, lse_parts=None,
+                     stream=None):
+    """Per-chunk partial results: O_parts [n,B,H,S_q,D_v] and LSE_parts
+    [n,B,H,S_q], both float32; chunk s covers keys kv_begin + s*split_len
+    onwards (split_len keys, cut to the range)."""
+    import torch
+
+    code, B, H, S_q, S_k, D_qk, D_v = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_qk)
+    o_parts = _buffer(o_parts, (n_splits, B, H, S_q, D_v), torch.float32, q, "o_parts")
+    lse_parts = _buffer(lse_parts, (n_splits, B, H, S_q), torch.float32, q, "lse_parts")
+    mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
+    _check(attn_fwd_partial_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts.data_ptr(),
+                                lse_parts.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal,
+                                code, mask, n_splits, split_len, _stream(stream, q.device)))
+    return o_parts, lse_parts
+
+
+def attn_merge(o_parts, lse_parts, dtype=None, out=None, lse=None, stream=None):
+    """Merge partial results: o_parts [n,B,H,S_q,D_v], lse_parts [n,B,H,S_q]
+    (float32) -> O [B,H,S_q,D_v] (``dtype``, default float32), LSE [B,H,S_q]."""
+    import torch
+
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    dtype = torch.float32 if dtype is None else dtype
+    if o_parts.dim() != 5 or lse_parts.dim() != 4:
+        raise ValueError("o_parts must be [n,B,H,S_q,D_v] and lse_parts [n,B,H,S_q]")
+    n, B, H, S_q, D_v = o_parts.shape
+    for name, t in (("o_parts", o_parts), ("lse_parts", lse_parts)):
+        if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
+    if tuple(lse_parts.shape) != (n, B, H, S_q):
+        raise ValueError("lse_parts shape does not match o_parts")
+    out = _buffer(out, (B, H, S_q, D_v), dtype, o_parts, "out")
+    lse = _buffer(lse, (B, H, S_q), torch.float32, o_parts, "lse")
+    _check(attn_merge_raw(o_parts.data_ptr(), lse_parts.data_ptr(), n, B, H, S_q, D_v,
+                          out.data_ptr(), lse.data_ptr(), codes[dtype],
+                          _stream(stream, o_parts.device)))
+    return out, lse
+
+
+def attn_fwd_splitkv(q, k, v, scale=None, causal=False, causal_offset=0, window=0, kv_begin=0,
+                     kv_end=None, n_splits=0, workspace=None, out=None, lse=None, stream=None):
+    """attn_fwd_ext computed over key chunks and merged (n_splits <= 0: the
+    library's choice).  ``workspace``: a uint8 GPU tensor of at least the
+    planned size (allocated here when None)."""
+    import torch
+
+    code, B, H, S_q, S_k, D_qk, D_v = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_qk)
+    out = _buffer(out, (B, H, S_q, D_v), q.dtype, q, "out")
+    lse = _buffer(lse, (B, H, S_q), torch.float32, q, "lse")
+    mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
+    _, _, ws = attn_splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal, code, mask, n_splits)
+    if workspace is None and ws > 0:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(attn_fwd_splitkv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal, code,
+                                mask, n_splits, ws_ptr, ws_bytes, _stream(stream, q.device)))
+    return out, lse
 
 
 def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None):

@@ -86,6 +86,145 @@ bool vector_dims_ok(int dtype, int64_t D_qk, int64_t D_v)
     return D_qk % per16 == 0 && D_v % per16 == 0;
 }
 
+// Kernel arguments common to every attention launch: sizes, the plan's
+// grid mapping, the scale folded into Q, and the default key visibility
+// (every key, plain causal).
+tsd::KernelArgs base_args(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                          int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v, float scale,
+                          int dtype, bool vec, const tsd_plan &plan)
+{
+    tsd::KernelArgs a;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = O;
+    a.LSE = LSE;
+    a.S_q = (int32_t)S_q;
+    a.S_k = (int32_t)S_k;
+    a.D_qk = (int32_t)D_qk;
+    a.D_v = (int32_t)D_v;
+    a.q_blocks = (int32_t)plan.q_blocks;
+    a.slices = (int32_t)plan.slices;
+    a.order = plan.order;
+    a.per_xcd = (int32_t)(plan.slices / 8);
+    // exp(x) = 2^(x log2 e): the log2(e) factor is folded into the scale.
+    // A negative scale becomes a sign flip of Q (exact) with |scale|; a zero
+    // scale makes every score 0, which is Q = 0 with any positive factor.
+    const float log2e = 1.4426950408889634f;
+    const uint32_t sign = dtype == TSD_F32 ? 0x80000000u : 0x80008000u;
+    a.c = scale == 0.0f ? 1.0f : std::fabs(scale) * log2e;
+    a.q_xor = scale < 0.0f ? sign : 0u;
+    a.q_and = scale == 0.0f ? 0u : 0xffffffffu;
+    a.vec = vec ? 1 : 0;
+    a.kv_begin = 0;
+    a.kv_end = (int32_t)S_k;
+    a.coff = 0;
+    a.window = 0;
+    a.splits = 1;
+    a.split_len = (int32_t)S_k;
+    a.part_o_stride = 0;
+    a.part_lse_stride = 0;
+    return a;
+}
+
+// Limits of the mask parameters: every per-row bound the kernel forms
+// (i + offset - window + 1, i + offset + 1) stays inside int32.
+constexpr int64_t kMaxMaskValue = int64_t(1) << 30;
+
+// Validate a key mask (NULL = every key, no offset, no window) against S_k.
+int check_mask(const tsd_mask *mask, int64_t S_k, tsd_mask *out)
+{
+    tsd_mask m = {0, 0, 0, S_k};
+    if (mask) m = *mask;
+    if (m.kv_begin < 0 || m.kv_end > S_k || m.kv_begin > m.kv_end || m.window < 0)
+        return TSD_ERR_SHAPE;
+    if (m.causal_offset > kMaxMaskValue || m.causal_offset < -kMaxMaskValue ||
+        m.window > kMaxMaskValue)
+        return TSD_ERR_UNSUPPORTED;
+    *out = m;
+    return TSD_OK;
+}
+
+// Checks shared by the extended entry points (which run on the LDS-direct
+// kernel only): 16-bit dtype, 16-byte aligned Q/K/V, widths a multiple of 8.
+int check_ext_inputs(const void *Q, const void *K, const void *V, int64_t B, int64_t H,
+                     int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v, float scale,
+                     int dtype)
+{
+    if (!Q || !K || !V) return TSD_ERR_NULL;
+    const int st = check_shape(B, H, S_q, S_k, D_qk, D_v, dtype);
+    if (st != TSD_OK) return st;
+    if (!std::isfinite(scale)) return TSD_ERR_SCALE;
+    if (dtype == TSD_F32) return TSD_ERR_UNSUPPORTED;
+    if (!vector_dims_ok(dtype, D_qk, D_v)) return TSD_ERR_UNSUPPORTED;
+    for (uintptr_t p : {(uintptr_t)Q, (uintptr_t)K, (uintptr_t)V})
+        if (p % 16 != 0) return TSD_ERR_UNSUPPORTED;
+    return TSD_OK;
+}
+
+// Byte sizes of the inputs (for the alias checks).
+struct InputBytes {
+    uint64_t q, k, v;
+};
+InputBytes input_bytes(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk,
+                       int64_t D_v, int dtype)
+{
+    const uint64_t elt = (uint64_t)elt_bytes(dtype), BH = (uint64_t)B * (uint64_t)H;
+    return InputBytes{BH * S_q * D_qk * elt, BH * S_k * D_qk * elt, BH * S_k * D_v * elt};
+}
+
+bool overlaps_inputs(const void *p, uint64_t n, const void *Q, const void *K, const void *V,
+                     const InputBytes &ib)
+{
+    return overlap(p, n, Q, ib.q) || overlap(p, n, K, ib.k) || overlap(p, n, V, ib.v);
+}
+
+// Launch the extended kernel over `splits` chunks of `split_len` keys
+// starting at mask.kv_begin (splits = 1: the whole range).  out_f32: O and
+// LSE are the chunked f32 partial buffers.
+int launch_ext(const void *Q, const void *K, const void *V, void *O, float *LSE, int64_t B,
+               int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v, float scale,
+               int causal, int dtype, const tsd_mask &mk, int64_t splits, int64_t split_len,
+               bool out_f32, hipStream_t stream)
+{
+    tsd_plan plan;
+    fill_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, true, &plan);
+    if (plan.grid > INT32_MAX / splits) return TSD_ERR_UNSUPPORTED;
+    tsd::KernelArgs a = base_args(Q, K, V, O, LSE, S_q, S_k, D_qk, D_v, scale, dtype, true, plan);
+    a.kv_begin = (int32_t)mk.kv_begin;
+    a.kv_end = (int32_t)mk.kv_end;
+    a.coff = (int32_t)mk.causal_offset;
+    a.window = (int32_t)mk.window;
+    a.splits = (int32_t)splits;
+    a.split_len = (int32_t)split_len;
+    if (out_f32) {
+        a.part_o_stride = plan.slices * S_q * D_v;
+        a.part_lse_stride = plan.slices * S_q;
+    }
+    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, true);
+    const hipError_t err = tsd::launch_attn_ext(cfg, dtype, causal != 0, out_f32,
+                                                plan.grid * splits, a, stream);
+    return err == hipSuccess ? TSD_OK : TSD_ERR_HIP;
+}
+
+// Split count chosen when the caller passes n_splits <= 0: enough chunks
+// that the grid covers the chip about twice (256 CUs, one workgroup per CU
+// for wide heads and three for narrow ones), with chunks of at least
+// kMinSplitKeys keys so that the pipeline prologue and the merge stay small
+// next to the chunk's own work.
+constexpr int64_t kMinSplitKeys = 512;
+constexpr int64_t kMaxSplits = 256;
+
+int64_t auto_splits(const tsd_plan &plan, int64_t keys)
+{
+    const int64_t per_cu = plan.waves == 8 ? 1 : 3;
+    const int64_t want = (2 * 256 * per_cu + plan.grid - 1) / plan.grid;
+    int64_t cap = keys / kMinSplitKeys;
+    if (cap < 1) cap = 1;
+    if (cap > kMaxSplits) cap = kMaxSplits;
+    return want < 1 ? 1 : (want > cap ? cap : want);
+}
+
 }  // namespace
 
 extern "C" int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk,
@@ -151,35 +290,188 @@ extern "C" int attn_fwd(const void *Q, const void *K, const void *V, void *O, fl
     tsd_plan plan;
     const bool vec = aligned16 && vector_dims_ok(dtype, D_qk, D_v);
     fill_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, vec, &plan);
-
-    tsd::KernelArgs a;
-    a.Q = Q;
-    a.K = K;
-    a.V = V;
-    a.O = O;
-    a.LSE = LSE;
-    a.S_q = (int32_t)S_q;
-    a.S_k = (int32_t)S_k;
-    a.D_qk = (int32_t)D_qk;
-    a.D_v = (int32_t)D_v;
-    a.q_blocks = (int32_t)plan.q_blocks;
-    a.slices = (int32_t)plan.slices;
-    a.order = plan.order;
-    a.per_xcd = (int32_t)(plan.slices / 8);
-    // exp(x) = 2^(x log2 e): the log2(e) factor is folded into the scale.
-    // A negative scale becomes a sign flip of Q (exact) with |scale|; a zero
-    // scale makes every score 0, which is Q = 0 with any positive factor.
-    const float log2e = 1.4426950408889634f;
-    const uint32_t sign = dtype == TSD_F32 ? 0x80000000u : 0x80008000u;
-    a.c = scale == 0.0f ? 1.0f : std::fabs(scale) * log2e;
-    a.q_xor = scale < 0.0f ? sign : 0u;
-    a.q_and = scale == 0.0f ? 0u : 0xffffffffu;
-    a.vec = vec ? 1 : 0;
+    const tsd::KernelArgs a =
+        base_args(Q, K, V, O, LSE, S_q, S_k, D_qk, D_v, scale, dtype, vec, plan);
 
     const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, vec);
     hipError_t err = tsd::launch_attn(cfg, dtype, causal != 0, plan.grid, a,
                                       reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? TSD_OK : TSD_ERR_HIP;
+}
+
+extern "C" int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                            int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk,
+                            int64_t D_v, float scale, int causal, int dtype,
+                            const tsd_mask *mask, void *stream)
+{
+    int st = check_ext_inputs(Q, K, V, B, H, S_q, S_k, D_qk, D_v, scale, dtype);
+    if (st != TSD_OK) return st;
+    if (!O) return TSD_ERR_NULL;
+    tsd_mask mk;
+    if ((st = check_mask(mask, S_k, &mk)) != TSD_OK) return st;
+    if ((uintptr_t)O % 16 != 0 || (uintptr_t)LSE % 4 != 0) return TSD_ERR_UNSUPPORTED;
+    const InputBytes ib = input_bytes(B, H, S_q, S_k, D_qk, D_v, dtype);
+    const uint64_t rows = (uint64_t)B * H * S_q;
+    const uint64_t o_bytes = rows * D_v * 2, l_bytes = LSE ? rows * 4 : 0;
+    if (overlaps_inputs(O, o_bytes, Q, K, V, ib) || overlaps_inputs(LSE, l_bytes, Q, K, V, ib) ||
+        overlap(LSE, l_bytes, O, o_bytes))
+        return TSD_ERR_ALIAS;
+    return launch_ext(Q, K, V, O, LSE, B, H, S_q, S_k, D_qk, D_v, scale, causal, dtype, mk, 1,
+                      mk.kv_end - mk.kv_begin, false, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int attn_fwd_partial(const void *Q, const void *K, const void *V, float *O_parts,
+                                float *LSE_parts, int64_t B, int64_t H, int64_t S_q,
+                                int64_t S_k, int64_t D_qk, int64_t D_v, float scale,
+                                int causal, int dtype, const tsd_mask *mask, int64_t n_splits,
+                                int64_t split_len, void *stream)
+{
+    int st = check_ext_inputs(Q, K, V, B, H, S_q, S_k, D_qk, D_v, scale, dtype);
+    if (st != TSD_OK) return st;
+    if (!O_parts || !LSE_parts) return TSD_ERR_NULL;
+    tsd_mask mk;
+    if ((st = check_mask(mask, S_k, &mk)) != TSD_OK) return st;
+    if (n_splits < 1 || split_len < 1) return TSD_ERR_SHAPE;
+    // chunk bounds kv_begin + s * split_len stay inside int32
+    if (split_len > INT32_MAX || n_splits > (INT32_MAX - mk.kv_begin) / split_len)
+        return TSD_ERR_UNSUPPORTED;
+    if (S_q > kMaxSliceBytes / (D_v * 4)) return TSD_ERR_UNSUPPORTED;   // f32 slice of O
+    if ((uintptr_t)O_parts % 16 != 0 || (uintptr_t)LSE_parts % 4 != 0)
+        return TSD_ERR_UNSUPPORTED;
+    const InputBytes ib = input_bytes(B, H, S_q, S_k, D_qk, D_v, dtype);
+    const uint64_t rows = (uint64_t)B * H * S_q;
+    const uint64_t o_bytes = (uint64_t)n_splits * rows * D_v * 4;
+    const uint64_t l_bytes = (uint64_t)n_splits * rows * 4;
+    if (overlaps_inputs(O_parts, o_bytes, Q, K, V, ib) ||
+        overlaps_inputs(LSE_parts, l_bytes, Q, K, V, ib) ||
+        overlap(LSE_parts, l_bytes, O_parts, o_bytes))
+        return TSD_ERR_ALIAS;
+    return launch_ext(Q, K, V, O_parts, LSE_parts, B, H, S_q, S_k, D_qk, D_v, scale, causal,
+                      dtype, mk, n_splits, split_len, true, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
+                          int64_t B, int64_t H, int64_t S_q, int64_t D_v, void *O, float *LSE,
+                          int dtype, void *stream)
+{
+    if (!O_parts || !LSE_parts || !O) return TSD_ERR_NULL;
+    if (n_parts < 1 || B < 1 || H < 1 || S_q < 1 || D_v < 1) return TSD_ERR_SHAPE;
+    const int elt = elt_bytes(dtype);
+    if (elt == 0 || D_v > kMaxHeadDim || n_parts > INT32_MAX) return TSD_ERR_UNSUPPORTED;
+    if (B > INT32_MAX / H || B * H > (INT64_MAX / 1024) / S_q) return TSD_ERR_UNSUPPORTED;
+    const int64_t rows = B * H * S_q;
+    if (n_parts > (INT64_MAX / 1024) / rows) return TSD_ERR_UNSUPPORTED;
+    const int64_t groups = (D_v + 3) / 4;
+    if ((rows * groups + 255) / 256 > INT32_MAX) return TSD_ERR_UNSUPPORTED;
+    if ((uintptr_t)O_parts % 4 != 0 || (uintptr_t)LSE_parts % 4 != 0 ||
+        (uintptr_t)O % elt != 0 || (uintptr_t)LSE % 4 != 0)
+        return TSD_ERR_UNSUPPORTED;
+    const uint64_t po = (uint64_t)n_parts * rows * D_v * 4, pl = (uint64_t)n_parts * rows * 4;
+    const uint64_t o_bytes = (uint64_t)rows * D_v * elt, l_bytes = LSE ? (uint64_t)rows * 4 : 0;
+    if (overlap(O, o_bytes, O_parts, po) || overlap(O, o_bytes, LSE_parts, pl) ||
+        overlap(LSE, l_bytes, O_parts, po) || overlap(LSE, l_bytes, LSE_parts, pl) ||
+        overlap(LSE, l_bytes, O, o_bytes))
+        return TSD_ERR_ALIAS;
+    tsd::MergeArgs a;
+    a.O_parts = O_parts;
+    a.LSE_parts = LSE_parts;
+    a.O = O;
+    a.LSE = LSE;
+    a.rows = rows;
+    a.part_o_stride = rows * D_v;
+    a.part_lse_stride = rows;
+    a.D_v = (int32_t)D_v;
+    a.n_parts = (int32_t)n_parts;
+    a.groups = (int32_t)groups;
+    const bool vec = D_v % 4 == 0 && (uintptr_t)O_parts % 16 == 0 &&
+                     (uintptr_t)O % (4 * elt) == 0;
+    const hipError_t err =
+        tsd::launch_merge(dtype, vec, a, reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? TSD_OK : TSD_ERR_HIP;
+}
+
+namespace {
+
+// Workspace layout of attn_fwd_splitkv: the f32 partial O of every chunk,
+// then (at a 256-byte boundary) the partial LSE.
+int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
+
+int splitkv_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
+                 int causal, int dtype, const tsd_mask &mk, int64_t n_splits,
+                 int64_t *splits_out, int64_t *split_len_out, int64_t *ws_out)
+{
+    tsd_plan plan;
+    fill_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, true, &plan);
+    const int64_t keys = mk.kv_end - mk.kv_begin;
+    int64_t n = n_splits > 0 ? n_splits : auto_splits(plan, keys);
+    if (n > kMaxSplits) return TSD_ERR_UNSUPPORTED;
+    // chunks of whole key tiles; no chunk past the range
+    int64_t len = keys > 0 ? (keys + n - 1) / n : 64;
+    len = (len + 63) / 64 * 64;
+    if (keys > 0) n = (keys + len - 1) / len;
+    if (n > (INT32_MAX - mk.kv_begin) / len) return TSD_ERR_UNSUPPORTED;
+    if (n > 1 && S_q > kMaxSliceBytes / (D_v * 4)) return TSD_ERR_UNSUPPORTED;
+    const int64_t rows = B * H * S_q;
+    *splits_out = n;
+    *split_len_out = len;
+    *ws_out = n > 1 ? round256(n * rows * D_v * 4) + round256(n * rows * 4) : 0;
+    return TSD_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_splitkv_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk,
+                                 int64_t D_v, int causal, int dtype, const tsd_mask *mask,
+                                 int64_t n_splits, int64_t *splits_out, int64_t *split_len_out,
+                                 int64_t *workspace_bytes)
+{
+    if (!splits_out || !split_len_out || !workspace_bytes) return TSD_ERR_NULL;
+    int st = check_shape(B, H, S_q, S_k, D_qk, D_v, dtype);
+    if (st != TSD_OK) return st;
+    if (dtype == TSD_F32 || !vector_dims_ok(dtype, D_qk, D_v)) return TSD_ERR_UNSUPPORTED;
+    tsd_mask mk;
+    if ((st = check_mask(mask, S_k, &mk)) != TSD_OK) return st;
+    return splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, mk, n_splits, splits_out,
+                        split_len_out, workspace_bytes);
+}
+
+extern "C" int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O,
+                                float *LSE, int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                                int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+                                const tsd_mask *mask, int64_t n_splits, void *workspace,
+                                int64_t workspace_bytes, void *stream)
+{
+    int st = check_ext_inputs(Q, K, V, B, H, S_q, S_k, D_qk, D_v, scale, dtype);
+    if (st != TSD_OK) return st;
+    if (!O) return TSD_ERR_NULL;
+    tsd_mask mk;
+    if ((st = check_mask(mask, S_k, &mk)) != TSD_OK) return st;
+    int64_t n = 0, len = 0, ws = 0;
+    if ((st = splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, mk, n_splits, &n, &len,
+                           &ws)) != TSD_OK)
+        return st;
+    if (n == 1)
+        return attn_fwd_ext(Q, K, V, O, LSE, B, H, S_q, S_k, D_qk, D_v, scale, causal, dtype,
+                            &mk, stream);
+    if (!workspace) return TSD_ERR_NULL;
+    if (workspace_bytes < ws) return TSD_ERR_SHAPE;
+    if ((uintptr_t)workspace % 256 != 0) return TSD_ERR_UNSUPPORTED;
+    if ((uintptr_t)O % 16 != 0 || (uintptr_t)LSE % 4 != 0) return TSD_ERR_UNSUPPORTED;
+    const InputBytes ib = input_bytes(B, H, S_q, S_k, D_qk, D_v, dtype);
+    const uint64_t rows = (uint64_t)B * H * S_q;
+    const uint64_t o_bytes = rows * D_v * 2, l_bytes = LSE ? rows * 4 : 0;
+    if (overlaps_inputs(O, o_bytes, Q, K, V, ib) || overlaps_inputs(LSE, l_bytes, Q, K, V, ib) ||
+        overlap(LSE, l_bytes, O, o_bytes) || overlaps_inputs(workspace, ws, Q, K, V, ib) ||
+        overlap(workspace, ws, O, o_bytes) || overlap(workspace, ws, LSE, l_bytes))
+        return TSD_ERR_ALIAS;
+    float *o_parts = static_cast<float *>(workspace);
+    float *l_parts = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
+                                               round256((int64_t)(n * rows * D_v * 4)));
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    st = launch_ext(Q, K, V, o_parts, l_parts, B, H, S_q, S_k, D_qk, D_v, scale, causal, dtype,
+                    mk, n, len, true, s);
+    if (st != TSD_OK) return st;
+    return attn_merge(o_parts, l_parts, n, B, H, S_q, D_v, O, LSE, dtype, stream);
 }
 
 extern "C" const char *attn_status_string(int status)

@@ -860,7 +860,12 @@ __device__ inline void wait_loads()
                                (15 << 8));
 }
 
-template <int DQ, int DV, bool CAUSAL, bool BF16>
+// EXT: the key range [kv_begin, kv_end) (optionally cut into `splits`
+// chunks, one per group of workgroups), a signed causal offset and a
+// window; rows that see no key get O = 0 and LSE = -inf.  OUT_F32: O is
+// written as f32 (partial results for a merge), chunk s at O + s *
+// part_o_stride and LSE + s * part_lse_stride.
+template <int DQ, int DV, bool CAUSAL, bool BF16, bool EXT = false, bool OUT_F32 = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(Fast16<DQ, DV>::THREADS,
                                                            Fast16<DQ, DV>::THREADS),
                                amdgpu_waves_per_eu(Fast16<DQ, DV>::SH.occ,
@@ -869,6 +874,7 @@ attn_fwd_fast16(KernelArgs p)
 {
     using T = Fast16<DQ, DV>;
     constexpr int BN = T::BN;
+    static_assert(EXT || !OUT_F32, "f32 output only in the extended kernel");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -876,16 +882,38 @@ attn_fwd_fast16(KernelArgs p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
 
-    int32_t qb, slice;
-    map_block((int32_t)blockIdx.x, p.q_blocks, p.slices, p.order, p.per_xcd, CAUSAL, qb, slice);
+    int32_t qb, slice, split = 0;
+    int32_t blk = (int32_t)blockIdx.x;
+    if constexpr (EXT) {
+        const int32_t per_split = p.q_blocks * p.slices;
+        split = blk / per_split;
+        blk -= split * per_split;
+    }
+    map_block(blk, p.q_blocks, p.slices, p.order, p.per_xcd, CAUSAL, qb, slice);
     const int q0 = qb * T::BM;
     const int qw = q0 + wave * 32;          // first query row of this wave
     const int qi = qw + l32;                // this lane's query row
+    // this workgroup's key range: everything, or one chunk of [kv_begin, kv_end)
+    int32_t klo = 0, khi = p.S_k;
+    if constexpr (EXT) {
+        klo = p.kv_begin + split * p.split_len;
+        khi = min(p.kv_end, klo + p.split_len);
+    }
+
+    // key tiles of this workgroup: t_first .. t_first + ntiles - 1
+    int t_first = 0, ntiles;
+    if constexpr (EXT) {
+        const KeyRange kr = wg_key_range(q0, min(q0 + T::BM, p.S_q), klo, khi, CAUSAL, p.coff,
+                                         p.window);
+        t_first = kr.key_lo / BN;
+        ntiles = kr.key_hi > kr.key_lo ? (kr.key_hi + BN - 1) / BN - t_first : 0;
+    } else {
+        ntiles = kv_tiles_for(qb, T::BM, BN, p.S_q, p.S_k, CAUSAL);
+    }
 
     const uint32_t q_bytes = (uint32_t)p.S_q * p.D_qk * 2;
     const uint32_t k_bytes = (uint32_t)p.S_k * p.D_qk * 2;
     const uint32_t v_bytes = (uint32_t)p.S_k * p.D_v * 2;
-    const uint32_t o_bytes = (uint32_t)p.S_q * p.D_v * 2;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(static_cast<const uint8_t *>(p.Q) + (size_t)slice * q_bytes, q_bytes);
     const u32x4 rk = rsrc_words(static_cast<const uint8_t *>(p.K) + (size_t)slice * k_bytes, k_bytes);
@@ -916,18 +944,52 @@ attn_fwd_fast16(KernelArgs p)
     // check still drops rows past the slice.
     auto issue_k = [&](int t, auto slot_c) __attribute__((always_inline)) {
         constexpr uint32_t sl = decltype(slot_c)::value * T::KT;
-        const u32x4 r = tile_rsrc(rk, (uint32_t)t * BN * p.D_qk * 2);
+        const u32x4 r = tile_rsrc(rk, (uint32_t)(t_first + t) * BN * p.D_qk * 2);
 #pragma unroll
         for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + sl + j * 1024, koff[j], r);
     };
     auto issue_v = [&](int t, auto slot_c) __attribute__((always_inline)) {
         constexpr uint32_t sl = decltype(slot_c)::value * T::VT;
-        const u32x4 r = tile_rsrc(rv, (uint32_t)t * BN * p.D_v * 2);
+        const u32x4 r = tile_rsrc(rv, (uint32_t)(t_first + t) * BN * p.D_v * 2);
 #pragma unroll
         for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + sl + j * 1024, voff[j], r);
     };
 
-    const int ntiles = kv_tiles_for(qb, T::BM, BN, p.S_q, p.S_k, CAUSAL);
+    // Output of this slice (of chunk `split` when the output is partial).
+    constexpr uint32_t o_elt = OUT_F32 ? 4u : 2u;
+    const uint32_t o_bytes = (uint32_t)p.S_q * p.D_v * o_elt;
+    auto out_rsrc = [&]() __attribute__((always_inline)) {
+        uint8_t *base = static_cast<uint8_t *>(p.O) + (size_t)slice * o_bytes;
+        if constexpr (OUT_F32) base += (size_t)split * p.part_o_stride * 4;
+        return make_rsrc(base, o_bytes);
+    };
+    auto lse_at = [&](int row) __attribute__((always_inline)) -> float & {
+        size_t idx = (size_t)slice * p.S_q + row;
+        if constexpr (OUT_F32) idx += (size_t)split * p.part_lse_stride;
+        return p.LSE[idx];
+    };
+    if constexpr (EXT) {
+        if (ntiles == 0) {
+            // no row of the workgroup sees a key: O = 0, LSE = -inf
+            const __amdgpu_buffer_rsrc_t ro0 = out_rsrc();
+            const bool ok = qi < p.S_q;
+#pragma unroll
+            for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d0 = d * 32 + g4 * 8 + hh * 4;
+                    const uint32_t off = (ok && d0 < p.D_v) ? (uint32_t)(qi * p.D_v + d0) * o_elt
+                                                            : kOutOfRange;
+                    if constexpr (OUT_F32)
+                        __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, ro0, off, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{0u, 0u}, ro0, off, 0, 0);
+                }
+            if (p.LSE && hh == 0 && ok) lse_at(qi) = neg_inf();
+            return;
+        }
+    }
+
     // Prologue: K(0 .. KS-1) and V(0 .. VS-2) in the order the main loop
     // would have issued them (K(j) before V(j-1)), K(0) first.
     issue_k(0, IC<0>{});
@@ -1041,6 +1103,20 @@ attn_fwd_fast16(KernelArgs p)
         }
     };
 
+    // Visible keys of this lane, [lo_i, hi_i), and of the wave: a tile needs
+    // no mask when it lies inside every row's range, and the wave is idle
+    // on a tile outside every row's range.
+    int lo_i = 0, hi_i = 0, wave_lo_min = 0, wave_lo_max = 0, wave_hi_min = 0, wave_hi_max = 0;
+    if constexpr (EXT) {
+        const bool win = p.window > 0;
+        lo_i = win ? max(klo, qi + p.coff - p.window + 1) : klo;
+        hi_i = CAUSAL ? min(khi, qi + p.coff + 1) : khi;
+        wave_lo_min = win ? max(klo, qw + p.coff - p.window + 1) : klo;
+        wave_lo_max = win ? max(klo, qw + 31 + p.coff - p.window + 1) : klo;
+        wave_hi_min = CAUSAL ? min(khi, qw + p.coff + 1) : khi;
+        wave_hi_max = CAUSAL ? min(khi, qw + 31 + p.coff + 1) : khi;
+    }
+
     // ---- prologue: scores of tile 0.  K(0) was the first load issued; every
     // other prologue load may still be in flight when all of them exist.
     if (ntiles >= T::KS) wait_loads<(T::KS - 1) * T::K_PER_W + (T::VS - 1) * T::V_PER_W>();
@@ -1064,35 +1140,52 @@ attn_fwd_fast16(KernelArgs p)
         constexpr uint32_t so1 = (uint32_t)((u + 1) % T::KS) * T::KT;   // K slot of tile t+1
         f32x16(&s)[2] = sc[u & 1];
         f32x16(&sn)[2] = sc[(u + 1) & 1];
-        const int kbase = t * BN;
-        const bool active = !CAUSAL || kbase <= qw + 31;   // some key of tile t is visible
+        const int kbase = (t_first + t) * BN;
+        // some key of tile t is visible to some row of the wave
+        bool active;
+        if constexpr (EXT) active = kbase < wave_hi_max && kbase + BN > wave_lo_min;
+        else active = !CAUSAL || kbase <= qw + 31;
 
         float mx = mxs[u & 1];
         bool grow_any = grows[u & 1];
         if (active) {
-            // masks: keys >= S_k; keys after the query when causal
-            const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > qw);
+            // masks: keys >= S_k; keys after the query when causal (in the
+            // extended kernel: keys outside the row's [lo_i, hi_i))
+            bool need_mask;
+            if constexpr (EXT) need_mask = kbase < wave_lo_max || kbase + BN > wave_hi_min;
+            else need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > qw);
             if (need_mask) {
                 // Register r of block kb holds key kbase + hh*8 + kb*32 +
                 // (r/8)*16 + r%8; it is kept when that key is < S_k and,
                 // causal, <= the query: one per-lane limit against
-                // compile-time offsets.
-                int lim = p.S_k - 1;
-                if (CAUSAL) lim = min(lim, qi);
-                lim -= kbase + hh * 8;
+                // compile-time offsets (two limits in the extended kernel).
+                int lim, lim_lo = 0;
+                if constexpr (EXT) {
+                    lim = hi_i - 1 - kbase - hh * 8;
+                    lim_lo = lo_i - kbase - hh * 8;
+                } else {
+                    lim = p.S_k - 1;
+                    if (CAUSAL) lim = min(lim, qi);
+                    lim -= kbase + hh * 8;
+                }
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        s[kb][r] = (kb * 32 + (r >> 3) * 16 + (r & 7)) <= lim ? s[kb][r]
-                                                                            : neg_inf();
+                    for (int r = 0; r < 16; ++r) {
+                        const int off = kb * 32 + (r >> 3) * 16 + (r & 7);
+                        bool keep = off <= lim;
+                        if constexpr (EXT) keep = keep && off >= lim_lo;
+                        s[kb][r] = keep ? s[kb][r] : neg_inf();
+                    }
                 mx = max_halves(lane_max(s));
                 grow_any = __builtin_amdgcn_ballot_w64((mx - m) * c > kTau) != 0;
             }
             // running max; rescale only when a row's max grows by > 2^kTau
             if (grow_any) {
                 const float m_new = fmaxf(m, mx);
-                const float alpha = fast_exp2((m - m_new) * c);
+                float alpha = fast_exp2((m - m_new) * c);
+                if constexpr (EXT)
+                    if (m_new == neg_inf()) alpha = 1.0f;   // row still without keys
                 m = m_new;
                 l *= alpha;
 #pragma unroll
@@ -1110,9 +1203,23 @@ attn_fwd_fast16(KernelArgs p)
         __syncthreads();
         if (t + T::KS < ntiles) issue_k(t + T::KS, IC<u % T::KS>{});
         if (t + T::VS - 1 < ntiles) issue_v(t + T::VS - 1, IC<(u + T::VS - 1) % T::VS>{});
-        if (!active) return;   // this and every later tile is after all rows of the wave
+        if (!active) {
+            // With a window a wave can be idle on tile t and busy on t+1:
+            // then it still forms the scores of t+1 here.
+            if constexpr (EXT) {
+                const int kn = kbase + BN;
+                if (t + 1 < ntiles && kn < wave_hi_max && kn + BN > wave_lo_min) {
+                    scores(so1, sn);
+                    mxs[(u + 1) & 1] = max_halves(lane_max(sn));
+                    grows[(u + 1) & 1] = true;   // m is still -inf for this wave
+                }
+            }
+            return;   // without a window, every later tile is idle too
+        }
 
-        const float mc = m * c;
+        float mc = m * c;
+        if constexpr (EXT)
+            if (m == neg_inf()) mc = 0.0f;   // row without keys so far: every P is 0
         float rs = 0.0f;
         u32x4 pb0[2], pb1[2];
         // phase A: scores of tile t+1 (garbage past the last tile, unused) || P of block 0
@@ -1145,24 +1252,36 @@ attn_fwd_fast16(KernelArgs p)
 
     // ---- epilogue: O = O_acc / l, LSE = m*scale + ln(l)
     const float lt = sum_halves(l);
-    const float inv = 1.0f / lt;
-    const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(static_cast<uint8_t *>(p.O) + (size_t)slice * o_bytes, o_bytes);
+    float inv = 1.0f / lt;
+    if constexpr (EXT)
+        if (!(lt > 0.0f)) inv = 0.0f;   // no visible key: O = 0
+    const __amdgpu_buffer_rsrc_t ro = out_rsrc();
     const bool row_ok = qi < p.S_q;
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
             const int d0 = d * 32 + g4 * 8 + hh * 4;   // 4 consecutive dims
-            const uint32_t w0 = pack2<BF16>(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv);
-            const uint32_t w1 = pack2<BF16>(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv);
             const uint32_t off =
-                (row_ok && d0 < p.D_v) ? (uint32_t)(qi * p.D_v + d0) * 2 : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, u32x2{w0, w1}), ro,
-                                                  off, 0, 0);
+                (row_ok && d0 < p.D_v) ? (uint32_t)(qi * p.D_v + d0) * o_elt : kOutOfRange;
+            if constexpr (OUT_F32) {
+                const f32x4 v4 = {o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv,
+                                  o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv};
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v4), ro, off, 0,
+                                                       0);
+            } else {
+                const uint32_t w0 = pack2<BF16>(o[d][4 * g4] * inv, o[d][4 * g4 + 1] * inv);
+                const uint32_t w1 = pack2<BF16>(o[d][4 * g4 + 2] * inv, o[d][4 * g4 + 3] * inv);
+                __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, u32x2{w0, w1}),
+                                                      ro, off, 0, 0);
+            }
         }
-    if (p.LSE && hh == 0 && row_ok)
-        p.LSE[(size_t)slice * p.S_q + qi] = (m * c + __builtin_amdgcn_logf(lt)) * kLn2;
+    if (p.LSE && hh == 0 && row_ok) {
+        float lse = (m * c + __builtin_amdgcn_logf(lt)) * kLn2;
+        if constexpr (EXT)
+            if (!(lt > 0.0f)) lse = neg_inf();
+        lse_at(qi) = lse;
+    }
 }
 
 int pad_dim(int64_t d) { return d <= 64 ? 64 : 128; }
@@ -1185,6 +1304,99 @@ hipError_t dispatch_fast(int dtype, bool causal, int64_t grid, const KernelArgs 
                       : launch(attn_fwd_fast16<DQ, DV, false, true>, grid, a, s, threads);
     return causal ? launch(attn_fwd_fast16<DQ, DV, true, false>, grid, a, s, threads)
                   : launch(attn_fwd_fast16<DQ, DV, false, false>, grid, a, s, threads);
+}
+
+template <int DQ, int DV>
+hipError_t dispatch_fast_ext(int dtype, bool causal, bool out_f32, int64_t grid,
+                             const KernelArgs &a, hipStream_t s)
+{
+    constexpr int threads = Fast16<DQ, DV>::THREADS;
+    if (out_f32) {
+        if (dtype == TSD_BF16)
+            return causal
+                       ? launch(attn_fwd_fast16<DQ, DV, true, true, true, true>, grid, a, s, threads)
+                       : launch(attn_fwd_fast16<DQ, DV, false, true, true, true>, grid, a, s, threads);
+        return causal
+                   ? launch(attn_fwd_fast16<DQ, DV, true, false, true, true>, grid, a, s, threads)
+                   : launch(attn_fwd_fast16<DQ, DV, false, false, true, true>, grid, a, s, threads);
+    }
+    if (dtype == TSD_BF16)
+        return causal
+                   ? launch(attn_fwd_fast16<DQ, DV, true, true, true, false>, grid, a, s, threads)
+                   : launch(attn_fwd_fast16<DQ, DV, false, true, true, false>, grid, a, s, threads);
+    return causal
+               ? launch(attn_fwd_fast16<DQ, DV, true, false, true, false>, grid, a, s, threads)
+               : launch(attn_fwd_fast16<DQ, DV, false, false, true, false>, grid, a, s, threads);
+}
+
+// ====================================================================
+// Merge of partial results over key chunks (the continuation pass):
+// for each query row, LSE = ln sum_g exp(LSE_g) and O = sum_g
+// exp(LSE_g - LSE) O_g.  A chunk with LSE_g = -inf (no visible key)
+// contributes nothing; a row whose chunks are all empty gets O = 0 and
+// LSE = -inf.  One thread per (row, 4 consecutive output columns): every
+// thread reads the row's n LSE values (shared by the row's threads through
+// the cache) and its own 4 columns of each chunk, so each byte of the
+// partial outputs is read once.  Bound by HBM bandwidth.
+// ====================================================================
+constexpr int kMergeThreads = 256;
+
+template <int ODT, bool VEC>
+__global__ void __launch_bounds__(kMergeThreads) attn_merge_kernel(MergeArgs p)
+{
+    const int64_t g = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    const int64_t row = g / p.groups;
+    if (row >= p.rows) return;
+    const int d0 = (int)(g - row * p.groups) * 4;
+    constexpr float kLog2e = 1.4426950408889634f;
+
+    float mx = neg_inf();
+    for (int j = 0; j < p.n_parts; ++j) mx = fmaxf(mx, p.LSE_parts[j * p.part_lse_stride + row]);
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    float lse = neg_inf();
+    if (mx != neg_inf()) {
+        float sum = 0.0f;
+        for (int j = 0; j < p.n_parts; ++j) {
+            const float w = fast_exp2((p.LSE_parts[j * p.part_lse_stride + row] - mx) * kLog2e);
+            sum += w;
+            const float *src = p.O_parts + j * p.part_o_stride + row * p.D_v + d0;
+            if constexpr (VEC) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(src);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, x[e], acc[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (d0 + e < p.D_v) acc[e] = __builtin_fmaf(w, src[e], acc[e]);
+            }
+        }
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= inv;
+        lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+    }
+    if (p.LSE && d0 == 0) p.LSE[row] = lse;
+    if constexpr (ODT == TSD_F32) {
+        float *dst = static_cast<float *>(p.O) + row * p.D_v + d0;
+        if constexpr (VEC) {
+            *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (d0 + e < p.D_v) dst[e] = acc[e];
+        }
+    } else {
+        constexpr bool BF = ODT == TSD_BF16;
+        uint16_t *dst = static_cast<uint16_t *>(p.O) + row * p.D_v + d0;
+        if constexpr (VEC) {
+            *reinterpret_cast<u32x2 *>(dst) =
+                u32x2{pack2<BF>(acc[0], acc[1]), pack2<BF>(acc[2], acc[3])};
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (d0 + e < p.D_v) dst[e] = (uint16_t)(pack2<BF>(acc[e], 0.0f) & 0xffffu);
+        }
+    }
 }
 
 template <int DQ, int DV>
@@ -1230,6 +1442,33 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec)
         t.lds_bytes = 2 * (64 * t.dqk_block + t.dv_block * 64) * 2;
     }
     return t;
+}
+
+hipError_t launch_attn_ext(const TileConfig &cfg, int dtype, bool causal, bool out_f32,
+                           int64_t grid, const KernelArgs &args, hipStream_t stream)
+{
+    if (!cfg.fast) return hipErrorInvalidValue;
+    switch ((cfg.dqk_block == 128 ? 2 : 0) + (cfg.dv_block == 128 ? 1 : 0)) {
+    case 0: return dispatch_fast_ext<64, 64>(dtype, causal, out_f32, grid, args, stream);
+    case 1: return dispatch_fast_ext<64, 128>(dtype, causal, out_f32, grid, args, stream);
+    case 2: return dispatch_fast_ext<128, 64>(dtype, causal, out_f32, grid, args, stream);
+    default: return dispatch_fast_ext<128, 128>(dtype, causal, out_f32, grid, args, stream);
+    }
+}
+
+hipError_t launch_merge(int dtype, bool vec, const MergeArgs &args, hipStream_t stream)
+{
+    const int64_t threads = args.rows * args.groups;
+    const int64_t grid = (threads + kMergeThreads - 1) / kMergeThreads;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((uint32_t)grid), dim3(kMergeThreads), 0, stream, args);
+        return hipGetLastError();
+    };
+    if (dtype == TSD_F32)
+        return vec ? go(attn_merge_kernel<TSD_F32, true>) : go(attn_merge_kernel<TSD_F32, false>);
+    if (dtype == TSD_BF16)
+        return vec ? go(attn_merge_kernel<TSD_BF16, true>) : go(attn_merge_kernel<TSD_BF16, false>);
+    return vec ? go(attn_merge_kernel<TSD_F16, true>) : go(attn_merge_kernel<TSD_F16, false>);
 }
 
 hipError_t launch_attn(const TileConfig &cfg, int dtype, bool causal, int64_t grid,

@@ -26,7 +26,34 @@ struct KernelArgs {
     uint32_t q_xor;    // XOR applied to every Q storage word (sign flip)
     uint32_t q_and;    // AND applied to every Q storage word (0 zeroes Q)
     int32_t vec;       // 1: 16-byte global accesses are legal
+    // Key visibility of the extended kernels (see KeyRange); the plain
+    // kernels use kv_begin = 0, kv_end = S_k, coff = 0, window = 0.
+    int32_t kv_begin, kv_end;   // key range [kv_begin, kv_end)
+    int32_t coff;               // causal: key j visible iff j <= i + coff
+    int32_t window;             // > 0: also j > i + coff - window
+    int32_t splits;             // key range cut into `splits` chunks ...
+    int32_t split_len;          // ... of split_len keys (a multiple of 64)
+    int64_t part_o_stride;      // elements between consecutive chunks' O (f32 output)
+    int64_t part_lse_stride;    // elements between consecutive chunks' LSE
 };
+
+// Keys a workgroup of query rows [q0, q_end) sees inside the key range
+// [klo, khi): row i sees [max(klo, i + coff - window + 1) (window > 0),
+// min(khi, i + coff + 1) (causal)); the workgroup's span is the union,
+// [key_lo, key_hi) (empty when key_hi <= key_lo).
+struct KeyRange {
+    int32_t key_lo, key_hi;
+};
+__host__ __device__ inline KeyRange wg_key_range(int32_t q0, int32_t q_end, int32_t klo,
+                                                 int32_t khi, bool causal, int32_t coff,
+                                                 int32_t window)
+{
+    int64_t lo = klo, hi = khi;
+    if (window > 0 && (int64_t)q0 + coff - window + 1 > lo) lo = (int64_t)q0 + coff - window + 1;
+    if (causal && (int64_t)q_end - 1 + coff + 1 < hi) hi = (int64_t)q_end - 1 + coff + 1;
+    if (hi < lo) hi = lo;
+    return KeyRange{(int32_t)lo, (int32_t)hi};
+}
 
 // Workgroup index -> (query block, slice).
 //
@@ -79,5 +106,25 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec);
 // Launch the kernel that matches (dtype, dqk_block, dv_block, causal).
 hipError_t launch_attn(const TileConfig &cfg, int dtype, bool causal, int64_t grid,
                        const KernelArgs &args, hipStream_t stream);
+
+// The extended form of the LDS-direct kernel (key range, offset, window,
+// key chunks; 16-bit or f32 output).  Grid: q_blocks * slices * splits.
+hipError_t launch_attn_ext(const TileConfig &cfg, int dtype, bool causal, bool out_f32,
+                           int64_t grid, const KernelArgs &args, hipStream_t stream);
+
+// Arguments of the merge of partial results over key chunks.
+struct MergeArgs {
+    const float *O_parts;     // [n_parts][rows][D_v] f32, chunk j at j * part_o_stride
+    const float *LSE_parts;   // [n_parts][rows] f32, chunk j at j * part_lse_stride
+    void *O;                  // [rows][D_v] of the output dtype
+    float *LSE;               // [rows] or null
+    int64_t rows;             // B * H * S_q
+    int64_t part_o_stride, part_lse_stride;
+    int32_t D_v, n_parts;
+    int32_t groups;           // ceil(D_v / 4) threads per row
+};
+
+// vec: D_v % 4 == 0 and the buffers allow 16-byte (f32) / 8-byte (16-bit) access.
+hipError_t launch_merge(int dtype, bool vec, const MergeArgs &args, hipStream_t stream);
 
 }  // namespace tsd
