@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
+    ap.add_argument("--n-splits", type=int, default=None,
+                    help="key chunks of a split-KV workload (default: the workload's)")
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="oracle sample: every N-th query row of every head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -117,10 +119,10 @@ def record_traffic(args) -> int:
     """Scale the attention kernel's FETCH_SIZE and WRITE_SIZE by what the same
     counters read for the copy probe (bytes known exactly) and store the
     result, keyed by workload and kernel source hash."""
-    from tiled_scaled_dot_amd.workloads import HEADLINE, WORKLOADS
+    from tiled_scaled_dot_amd.workloads import ALL_WORKLOADS, HEADLINE
 
     name = args.workload or HEADLINE
-    w = WORKLOADS[name]
+    w = ALL_WORKLOADS[name]
     a_fetch, a_write, c_fetch, c_write = args.record_traffic
     is_attn = lambda k: "attn_fwd" in k
     is_copy = lambda k: "attn_fwd" not in k
@@ -143,7 +145,7 @@ def record_traffic(args) -> int:
         "hbm_bytes_per_launch": round(read_b + write_b),
         "read_bytes": round(read_b),
         "write_bytes": round(write_b),
-        "algorithmic_bytes": w.min_bytes(),
+        "min_bytes_of_step": w.min_bytes(),
         "fetch_size_kib": fetch_kib,
         "write_size_kib": write_kib,
         "copy_probe_bytes": copy_bytes,
@@ -191,15 +193,24 @@ def cpu_baseline(w, q, k, v, stride: int):
 
     import oracle
 
-    rows = list(range(stride - 1, w.S_q, stride))
+    rows = list(range(stride - 1, w.S_q, stride)) or [0]
     qd = q.double().numpy()
     kd = k.double().numpy()
     vd = v.double().numpy()
     threads = oracle.default_threads()
+    ext = hasattr(w, "entry")
     t0 = time.perf_counter()
-    oracle.attn_ref(qd, kd, vd, w.scale, w.causal, rows=rows, nthreads=threads)
+    if ext:
+        oracle.attn_ref_ext(qd, kd, vd, w.scale, w.causal, causal_offset=w.causal_offset,
+                            window=w.window, rows=rows, nthreads=threads)
+    else:
+        oracle.attn_ref(qd, kd, vd, w.scale, w.causal, rows=rows, nthreads=threads)
     dt = time.perf_counter() - t0
-    pairs = sum((min(r + 1, w.S_k) if w.causal else w.S_k) for r in rows) * w.B * w.H
+    if ext:
+        lo, hi = w.row_ranges()
+        pairs = int(sum(hi[r] - lo[r] for r in rows)) * w.B * w.H
+    else:
+        pairs = sum((min(r + 1, w.S_k) if w.causal else w.S_k) for r in rows) * w.B * w.H
     flops = 2.0 * pairs * (w.D_qk + w.D_v)
     cpu_model = ""
     try:
@@ -215,7 +226,7 @@ def cpu_baseline(w, q, k, v, stride: int):
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"query rows i = {stride - 1} mod {stride} of all {w.B * w.H} slices "
+        "sample": (f"query rows i = {rows[0] % stride} mod {stride} of all {w.B * w.H} slices "
                    f"({len(rows)} rows/slice, {flops / 1e9:.1f} GFLOP of visible pairs, "
                    f"{dt:.1f} s, fp64, {cpu_model or platform.processor()})"),
     }
@@ -237,55 +248,110 @@ def main():
     import torch
 
     import tiled_scaled_dot_amd as tsd
-    from tiled_scaled_dot_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+    from tiled_scaled_dot_amd.workloads import ALL_WORKLOADS, HEADLINE, make_inputs
 
     name = args.workload or HEADLINE
-    w = WORKLOADS[name]
+    w = ALL_WORKLOADS[name]
+    if args.n_splits is not None:
+        if getattr(w, "entry", "fwd") != "splitkv":
+            raise SystemExit("--n-splits applies to split-KV workloads only")
+        w = w.with_(n_splits=args.n_splits)
     dev = torch.device("cuda:0")
     q, k, v = make_inputs(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     o = torch.empty(w.shape_o, dtype=qd.dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.S_q), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    flops = w.metric_flops()
+    min_bytes = w.min_bytes()
+    entry = getattr(w, "entry", "fwd")
+    extra = {}
+
+    # A step is a list of launches; the first is the attention kernel (the
+    # dominant one, the roofline's subject), with its algorithmic FLOPs and
+    # bytes per launch.
+    if entry == "fwd":
+        phases = [lambda: tsd.attn_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o,
+                                       lse=lse, stream=stream)]
+        attn_bytes = min_bytes
+    elif entry == "ext":
+        phases = [lambda: tsd.attn_fwd_ext(qd, kd, vd, scale=w.scale, causal=w.causal,
+                                           causal_offset=w.causal_offset, window=w.window,
+                                           out=o, lse=lse, stream=stream)]
+        attn_bytes = min_bytes
+    else:   # splitkv: partial results over key chunks, then the merge
+        mask = tsd.make_mask(w.S_k, w.causal_offset, w.window)
+        n, split_len, _ = tsd.attn_splitkv_plan(w.B, w.H, w.S_q, w.S_k, w.D_qk, w.D_v,
+                                                w.causal, w.dtype, mask, w.n_splits)
+        o_parts = torch.empty((n, w.B, w.H, w.S_q, w.D_v), dtype=torch.float32, device=dev)
+        l_parts = torch.empty((n, w.B, w.H, w.S_q), dtype=torch.float32, device=dev)
+        phases = [
+            lambda: tsd.attn_fwd_partial(qd, kd, vd, n, split_len, scale=w.scale,
+                                         causal=w.causal, causal_offset=w.causal_offset,
+                                         window=w.window, o_parts=o_parts,
+                                         lse_parts=l_parts, stream=stream),
+            lambda: tsd.attn_merge(o_parts, l_parts, dtype=qd.dtype, out=o, lse=lse,
+                                   stream=stream),
+        ]
+        rows = w.B * w.H * w.S_q
+        elt = qd.element_size()
+        part_bytes = n * rows * (w.D_v * 4 + 4)
+        # each chunk reads Q again and writes f32 partials instead of O
+        attn_bytes = (min_bytes - rows * (w.D_v * elt + 4) + (n - 1) * rows * w.D_qk * elt
+                      + part_bytes)
+        extra = {"n_splits": n, "split_len": split_len,
+                 "merge_bytes_per_launch": part_bytes + rows * (w.D_v * elt + 4)}
 
     def step():
-        tsd.attn_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o, lse=lse, stream=stream)
+        for ph in phases:
+            ph()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # events before every launch and after the last: per-launch durations
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
+        for j, ph in enumerate(phases):
+            ev[i][j].record(stream)
+            ph()
+        ev[i][-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     sclk_mhz = measure_sclk(step, torch)
 
-    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    launch_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps
+                 for j in range(len(phases))]
+    kernel_ms = launch_ms[0]
     ms_per_step = wall * 1e3 / args.steps
-    flops = w.metric_flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = stored_traffic(name)
-    # Roofline of the launch: MFMA when the metric FLOPs per minimum byte
-    # exceed the ridge (peak / HBM bandwidth), else HBM (small configs).
-    min_bytes = w.min_bytes()
+    # Roofline of the attention launch: MFMA when its FLOPs per algorithmic
+    # byte exceed the ridge (peak / HBM bandwidth), else HBM.
     ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if flops / min_bytes >= ridge:
+    if flops / attn_bytes >= ridge:
         bound, unit, roof_peak = "mfma", "TFLOP/s", peak
         achieved = flops / (kernel_ms * 1e-3) / 1e12
     else:
         bound, unit, roof_peak = "hbm", "GB/s", PEAK_HBM_GBS
-        achieved = min_bytes / (kernel_ms * 1e-3) / 1e9
+        achieved = attn_bytes / (kernel_ms * 1e-3) / 1e9
+    if len(phases) > 1:
+        extra["merge_ms"] = round(launch_ms[1], 4)
+        extra["merge_gbs"] = round(extra["merge_bytes_per_launch"] / (launch_ms[1] * 1e-3) / 1e9,
+                                   1)
+    if entry != "fwd":
+        extra.update(entry=entry, causal_offset=w.causal_offset, window=w.window,
+                     visible_pairs_per_slice=w.visible_pairs())
 
     result = {
-        "metric": "attention fwd TFLOP/s and % of MFMA peak (bf16 causal, S=16k, D=128)",
+        "metric": ("attention fwd TFLOP/s and % of MFMA peak (bf16 causal, S=16k, D=128)"
+                   if entry == "fwd" else
+                   "attention fwd TFLOP/s over visible (query, key) pairs"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -313,6 +379,8 @@ def main():
                 round(100.0 * (flops / (kernel_ms * 1e-3) / 1e12) / (peak * sclk_mhz / 2400.0), 2)
                 if sclk_mhz else None),
             "min_bytes_per_step": min_bytes,
+            "attn_bytes_per_launch": attn_bytes,
+            **extra,
             "device": torch.cuda.get_device_name(dev),
             "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
         },

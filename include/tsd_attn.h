@@ -206,8 +206,8 @@ int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
 
 /*
  * attn_splitkv_plan — the chunking attn_fwd_splitkv uses (host only).
- * n_splits <= 0 lets the library choose: enough chunks that the launch
- * covers the 256 compute units about twice, chunks of at least 512 keys,
+ * n_splits <= 0 lets the library choose: enough chunks that one round of
+ * workgroups covers the 256 compute units, chunks of at least 512 keys,
  * at most 256 chunks.  Reports the chunk count actually used (chunks are
  * whole 64-key tiles, so it may come out below the request), the chunk
  * length in keys and the workspace bytes attn_fwd_splitkv needs (0 when a

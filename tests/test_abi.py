@@ -290,11 +290,17 @@ def test_merge_rejects(lib):
 
 
 def test_splitkv_plan(lib):
-    # few query blocks, many keys: chunks until the grid covers the chip twice
+    # few query blocks, many keys: chunks until one round of workgroups
+    # covers the chip (one wide workgroup per CU)
     n, ln, ws = tsd.attn_splitkv_plan(1, 8, 512, 131072, 128, 128, False, "bf16")
     plan = tsd.attn_fwd_plan(1, 8, 512, 131072, 128, 128, False, "bf16")
-    assert plan.grid * n >= 512 and ln % 64 == 0 and n * ln >= 131072
+    assert plan.grid * n >= 256 and plan.grid * (n - 1) < 256
+    assert ln % 64 == 0 and n * ln >= 131072
     assert ws == math.ceil(n * 8 * 512 * 128 * 4 / 256) * 256 + math.ceil(n * 8 * 512 * 4 / 256) * 256
+    # narrow heads: three workgroups per CU
+    n, _, _ = tsd.attn_splitkv_plan(1, 8, 512, 131072, 64, 64, False, "bf16")
+    plan = tsd.attn_fwd_plan(1, 8, 512, 131072, 64, 64, False, "bf16")
+    assert plan.grid * n >= 768 and plan.grid * (n - 1) < 768
     # a full grid keeps one chunk and needs no workspace
     assert tsd.attn_splitkv_plan(4, 16, 4096, 4096, 128, 128, True, "bf16") == (1, 4096, 0)
     # requested counts: chunks are whole tiles and none lies past the range

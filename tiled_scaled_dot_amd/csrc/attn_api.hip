@@ -208,17 +208,18 @@ int launch_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
 }
 
 // Split count chosen when the caller passes n_splits <= 0: enough chunks
-// that the grid covers the chip about twice (256 CUs, one workgroup per CU
-// for wide heads and three for narrow ones), with chunks of at least
-// kMinSplitKeys keys so that the pipeline prologue and the merge stay small
-// next to the chunk's own work.
+// that one round of workgroups covers the chip (256 CUs, one workgroup per
+// CU for wide heads and three for narrow ones; measured on long-context
+// prefill and decoding, more chunks only add merge traffic and re-reads of
+// Q), with chunks of at least kMinSplitKeys keys so that the pipeline
+// prologue and the merge stay small next to the chunk's own work.
 constexpr int64_t kMinSplitKeys = 512;
 constexpr int64_t kMaxSplits = 256;
 
 int64_t auto_splits(const tsd_plan &plan, int64_t keys)
 {
     const int64_t per_cu = plan.waves == 8 ? 1 : 3;
-    const int64_t want = (2 * 256 * per_cu + plan.grid - 1) / plan.grid;
+    const int64_t want = (256 * per_cu + plan.grid - 1) / plan.grid;
     int64_t cap = keys / kMinSplitKeys;
     if (cap < 1) cap = 1;
     if (cap > kMaxSplits) cap = kMaxSplits;

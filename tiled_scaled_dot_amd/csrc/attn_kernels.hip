@@ -1115,6 +1115,7 @@ attn_fwd_fast16(KernelArgs p)
         wave_lo_max = win ? max(klo, qw + 31 + p.coff - p.window + 1) : klo;
         wave_hi_min = CAUSAL ? min(khi, qw + p.coff + 1) : khi;
         wave_hi_max = CAUSAL ? min(khi, qw + 31 + p.coff + 1) : khi;
+        if (qw >= p.S_q) wave_hi_max = -1;   // no row of the wave exists: idle throughout
     }
 
     // ---- prologue: scores of tile 0.  K(0) was the first load issued; every
@@ -1340,6 +1341,7 @@ hipError_t dispatch_fast_ext(int dtype, bool causal, bool out_f32, int64_t grid,
 // partial outputs is read once.  Bound by HBM bandwidth.
 // ====================================================================
 constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 8;
 
 template <int ODT, bool VEC>
 __global__ void __launch_bounds__(kMergeThreads) attn_merge_kernel(MergeArgs p)
@@ -1350,30 +1352,54 @@ __global__ void __launch_bounds__(kMergeThreads) attn_merge_kernel(MergeArgs p)
     const int d0 = (int)(g - row * p.groups) * 4;
     constexpr float kLog2e = 1.4426950408889634f;
 
-    float mx = neg_inf();
-    for (int j = 0; j < p.n_parts; ++j) mx = fmaxf(mx, p.LSE_parts[j * p.part_lse_stride + row]);
+    // One pass in batches of kMergeBatch chunks, all loads of a batch issued
+    // before any is used: a running max m, the sum of exp(LSE_g - m) and the
+    // weighted O, rescaled when m grows.
+    float m = neg_inf(), sum = 0.0f;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float lse = neg_inf();
-    if (mx != neg_inf()) {
-        float sum = 0.0f;
-        for (int j = 0; j < p.n_parts; ++j) {
-            const float w = fast_exp2((p.LSE_parts[j * p.part_lse_stride + row] - mx) * kLog2e);
-            sum += w;
-            const float *src = p.O_parts + j * p.part_o_stride + row * p.D_v + d0;
-            if constexpr (VEC) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(src);
+    for (int j0 = 0; j0 < p.n_parts; j0 += kMergeBatch) {
+        float lv[kMergeBatch];
+        f32x4 ov[kMergeBatch];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, x[e], acc[e]);
-            } else {
+        for (int b = 0; b < kMergeBatch; ++b) {
+            const int j = j0 + b;
+            lv[b] = neg_inf();
+            ov[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (j < p.n_parts) {
+                lv[b] = p.LSE_parts[j * p.part_lse_stride + row];
+                const float *src = p.O_parts + j * p.part_o_stride + row * p.D_v + d0;
+                if constexpr (VEC) {
+                    ov[b] = *reinterpret_cast<const f32x4 *>(src);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (d0 + e < p.D_v) acc[e] = __builtin_fmaf(w, src[e], acc[e]);
+                    for (int e = 0; e < 4; ++e)
+                        if (d0 + e < p.D_v) ov[b][e] = src[e];
+                }
             }
         }
+        float bm = m;
+#pragma unroll
+        for (int b = 0; b < kMergeBatch; ++b) bm = fmaxf(bm, lv[b]);
+        if (bm == neg_inf()) continue;   // no chunk so far sees a key
+        const float r = fast_exp2((m - bm) * kLog2e);   // 0 while m is -inf
+        sum *= r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= r;
+#pragma unroll
+        for (int b = 0; b < kMergeBatch; ++b) {
+            const float w = fast_exp2((lv[b] - bm) * kLog2e);   // 0 for an empty chunk
+            sum += w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, ov[b][e], acc[e]);
+        }
+        m = bm;
+    }
+    float lse = neg_inf();
+    if (m != neg_inf()) {
         const float inv = 1.0f / sum;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] *= inv;
-        lse = mx + __builtin_amdgcn_logf(sum) * kLn2;
+        lse = m + __builtin_amdgcn_logf(sum) * kLn2;
     }
     if (p.LSE && d0 == 0) p.LSE[row] = lse;
     if constexpr (ODT == TSD_F32) {

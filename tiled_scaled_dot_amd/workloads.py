@@ -117,6 +117,80 @@ WORKLOADS = {
 HEADLINE = "bf16_b1h32_s16384_d128_causal"
 
 
+@dataclass(frozen=True)
+class ExtWorkload(Workload):
+    """A workload of the extended entry points: row i sees the keys
+    [max(0, i + causal_offset - window + 1) if window else 0,
+     min(S_k, i + causal_offset + 1) if causal else S_k).
+    entry: "ext" (attn_fwd_ext, one launch) or "splitkv" (attn_fwd_partial
+    over key chunks, then attn_merge; n_splits 0 = the library's choice)."""
+    causal_offset: int = 0
+    window: int = 0
+    entry: str = "ext"
+    n_splits: int = 0
+
+    def row_ranges(self):
+        import numpy as np
+
+        i = np.arange(self.S_q, dtype=np.int64)
+        lo = np.zeros_like(i)
+        if self.window > 0:
+            lo = np.maximum(lo, i + self.causal_offset - self.window + 1)
+        hi = np.full_like(i, self.S_k)
+        if self.causal:
+            hi = np.minimum(hi, i + self.causal_offset + 1)
+        return lo, np.maximum(hi, lo)
+
+    def visible_pairs(self) -> int:
+        lo, hi = self.row_ranges()
+        return int((hi - lo).sum())
+
+    def metric_flops(self) -> float:
+        """2 * (D_qk + D_v) per visible (query, key) pair."""
+        return 2.0 * self.B * self.H * self.visible_pairs() * (self.D_qk + self.D_v)
+
+    def key_span(self) -> int:
+        lo, hi = self.row_ranges()
+        live = hi > lo
+        return int(hi[live].max() - lo[live].min()) if live.any() else 0
+
+    def min_bytes(self) -> int:
+        """Q, the keys and values some row sees, O (storage dtype) and LSE."""
+        elt = DTYPES[self.dtype].itemsize
+        per = elt * (self.S_q * self.D_qk + self.key_span() * (self.D_qk + self.D_v)
+                     + self.S_q * self.D_v) + 4 * self.S_q
+        return self.B * self.H * per
+
+
+def _x(name, B, H, S_q, S_k, D, causal, causal_offset, window, entry, seed, n_splits=0):
+    return ExtWorkload(name, "bf16", B, H, S_q, S_k, D, D, causal, 1.0 / math.sqrt(D),
+                       "normal", 1.0, 1.0, seed, causal_offset=causal_offset, window=window,
+                       entry=entry, n_splits=n_splits)
+
+
+# Workloads of the extended entry points (measured, not part of the target's
+# table): a chunk of 512 new queries against a 128k-key context and one
+# decoding query per sequence against 16k keys, both with the diagonal at
+# the bottom right, each with and without key chunks; and the long causal
+# case with a 4096-key sliding window.
+EXT_WORKLOADS = {
+    w.name: w for w in [
+        _x("bf16_b1h8_q512_k131072_d128_prefill_splitkv", 1, 8, 512, 131072, 128, True,
+           131072 - 512, 0, "splitkv", 6),
+        _x("bf16_b1h8_q512_k131072_d128_prefill_nosplit", 1, 8, 512, 131072, 128, True,
+           131072 - 512, 0, "ext", 6),
+        _x("bf16_b4h32_q1_k16384_d128_decode_splitkv", 4, 32, 1, 16384, 128, True,
+           16384 - 1, 0, "splitkv", 7),
+        _x("bf16_b4h32_q1_k16384_d128_decode_nosplit", 4, 32, 1, 16384, 128, True,
+           16384 - 1, 0, "ext", 7),
+        _x("bf16_b1h32_s16384_d128_causal_window4096", 1, 32, 16384, 16384, 128, True,
+           0, 4096, "ext", 8),
+    ]
+}
+
+ALL_WORKLOADS = {**WORKLOADS, **EXT_WORKLOADS}
+
+
 def make_inputs(w: Workload, device="cpu"):
     """Return (q, k, v) in the workload's storage dtype (CPU unless asked)."""
     g = torch.Generator(device="cpu").manual_seed(w.seed)
