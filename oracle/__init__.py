@@ -30,8 +30,11 @@ _lib = None
 
 
 def build(force: bool = True, source: str = SOURCE, output: str = LIBRARY) -> str:
-    """Compile the oracle with gcc (no fast-math: IEEE double semantics)."""
-    if force or not os.path.exists(output):
+    """Compile the oracle with gcc (no fast-math: IEEE double semantics);
+    without ``force`` only when the library is missing or older than the
+    source."""
+    if (force or not os.path.exists(output)
+            or os.path.getmtime(source) > os.path.getmtime(output)):
         tmp = output + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
                "-fno-fast-math", "-ffp-contract=off", source, "-o", tmp, "-lm"]
@@ -50,7 +53,7 @@ def load_library(path: str) -> ctypes.CDLL:
                   ctypes.c_int]
     f.restype = ctypes.c_int
     g = lib.attn_ref_ext_f64
-    g.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64,
+    g.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, i64,
                   ctypes.c_double, ctypes.c_int, i64, i64, i64, i64,
                   ctypes.POINTER(i64), i64, ctypes.c_int]
     g.restype = ctypes.c_int
@@ -120,15 +123,17 @@ def attn_ref_ext(q, k, v, scale: float, causal: bool, causal_offset: int = 0,
     """``attn_ref`` with each query row i restricted to the keys j with
     kv_begin <= j < kv_end, j <= i + causal_offset (causal) and
     j > i + causal_offset - window (window > 0).  Rows without a visible
-    key give O = 0 and LSE = -inf."""
+    key give O = 0 and LSE = -inf.  k and v may hold fewer heads than q
+    (H_kv dividing H): query head h then reads K/V head h // (H // H_kv)."""
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
     v = np.ascontiguousarray(v, dtype=np.float64)
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D [B,H,S,D]")
     B, H, S_q, D_qk = q.shape
-    if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != D_qk \
-            or v.shape[2] != k.shape[2]:
+    H_kv = k.shape[1]
+    if k.shape[0] != B or v.shape[:2] != (B, H_kv) or k.shape[3] != D_qk \
+            or v.shape[2] != k.shape[2] or H_kv < 1 or H % H_kv != 0:
         raise ValueError("inconsistent q/k/v shapes")
     S_k, D_v = k.shape[2], v.shape[3]
     if kv_end is None:
@@ -144,7 +149,8 @@ def attn_ref_ext(q, k, v, scale: float, causal: bool, causal_offset: int = 0,
     p = np.empty((B, H, n_rows, S_k), dtype=np.float64) if want_probs else None
     lib = lib or _library()
     rc = lib.attn_ref_ext_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(p),
-                              B, H, S_q, S_k, D_qk, D_v, float(scale), int(bool(causal)),
+                              B, H, H_kv, S_q, S_k, D_qk, D_v, float(scale),
+                              int(bool(causal)),
                               int(causal_offset), int(window), int(kv_begin), int(kv_end),
                               rows_p, n_rows, int(nthreads or default_threads()))
     if rc != 0:

@@ -47,6 +47,10 @@
  *     the diagonal).
  *   A row that sees no key gets O = 0 and LSE = -infinity (the neutral
  *   element of the merge).
+ *   It also takes grouped K/V heads: K and V hold H_kv heads (H a multiple
+ *   of H_kv) and query head h reads K/V head h / (H / H_kv), the key
+ *   address of attention_score on the same page (program p of batch p / H
+ *   reads K head (p mod H) / (H / H_KV)); H_kv = H is the plain layout.
  *
  * Layout: contiguous row-major Q[B,H,S_q,D_qk], K[B,H,S_k,D_qk],
  * V[B,H,S_k,D_v], O[B,H,S_q,D_v], LSE[B,H,S_q] (all double).
@@ -61,7 +65,7 @@
 typedef struct {
     const double *Q, *K, *V;
     double *O, *LSE, *P;
-    int64_t B, H, S_q, S_k, D_qk, D_v;
+    int64_t B, H, H_kv, S_q, S_k, D_qk, D_v;
     double scale;
     int causal;
     int64_t coff, window, kv_begin, kv_end;   /* key range of every row, see above */
@@ -76,8 +80,10 @@ static void oracle_row(const oracle_job *jb, int64_t slice, int64_t out_row,
                        int64_t i, double *s, double *w, double *acc)
 {
     const double *q = jb->Q + (slice * jb->S_q + i) * jb->D_qk;
-    const double *k = jb->K + slice * jb->S_k * jb->D_qk;
-    const double *v = jb->V + slice * jb->S_k * jb->D_v;
+    /* K/V head of this query head: H / H_kv consecutive query heads share one */
+    const int64_t kv_slice = (slice / jb->H) * jb->H_kv + (slice % jb->H) / (jb->H / jb->H_kv);
+    const double *k = jb->K + kv_slice * jb->S_k * jb->D_qk;
+    const double *v = jb->V + kv_slice * jb->S_k * jb->D_v;
 
     /* visible keys j in [lo, hi): the key range, then j <= i + coff when
        causal, then j > i + coff - window when windowed */
@@ -164,7 +170,8 @@ static void *oracle_worker(void *arg)
  * attn_ref_ext_f64: the definition above with each row's keys restricted to
  * [max(kv_begin, i + causal_offset - window + 1) (window > 0 only),
  *  min(kv_end, i + causal_offset + 1) (causal only)).
- * Requires 0 <= kv_begin <= kv_end <= S_k and window >= 0.
+ * Requires 0 <= kv_begin <= kv_end <= S_k, window >= 0 and H_kv >= 1
+ * dividing H; K is [B,H_kv,S_k,D_qk] and V [B,H_kv,S_k,D_v].
  *
  * Returns 0 on success, 1 for a bad argument (null pointer, a dimension
  * below 1, a row index outside [0, S_q), a key range outside [0, S_k]),
@@ -174,7 +181,7 @@ static void *oracle_worker(void *arg)
  */
 int attn_ref_ext_f64(const double *Q, const double *K, const double *V,
                      double *O, double *LSE, double *P,
-                     int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                     int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                      int64_t D_qk, int64_t D_v, double scale, int causal,
                      int64_t causal_offset, int64_t window, int64_t kv_begin,
                      int64_t kv_end, const int64_t *rows, int64_t n_rows, int nthreads)
@@ -184,6 +191,8 @@ int attn_ref_ext_f64(const double *Q, const double *K, const double *V,
     if (B < 1 || H < 1 || S_q < 1 || S_k < 1 || D_qk < 1 || D_v < 1)
         return 1;
     if (kv_begin < 0 || kv_end < kv_begin || kv_end > S_k || window < 0)
+        return 1;
+    if (H_kv < 1 || H % H_kv != 0)
         return 1;
     if (rows) {
         if (n_rows < 1)
@@ -212,7 +221,7 @@ int attn_ref_ext_f64(const double *Q, const double *K, const double *V,
         oracle_job *jb = &jobs[t];
         jb->Q = Q; jb->K = K; jb->V = V;
         jb->O = O; jb->LSE = LSE; jb->P = P;
-        jb->B = B; jb->H = H; jb->S_q = S_q; jb->S_k = S_k;
+        jb->B = B; jb->H = H; jb->H_kv = H_kv; jb->S_q = S_q; jb->S_k = S_k;
         jb->D_qk = D_qk; jb->D_v = D_v;
         jb->scale = scale; jb->causal = causal;
         jb->coff = causal_offset; jb->window = window;
@@ -248,6 +257,6 @@ int attn_ref_f64(const double *Q, const double *K, const double *V,
                  int64_t D_qk, int64_t D_v, double scale, int causal,
                  const int64_t *rows, int64_t n_rows, int nthreads)
 {
-    return attn_ref_ext_f64(Q, K, V, O, LSE, P, B, H, S_q, S_k, D_qk, D_v, scale, causal,
+    return attn_ref_ext_f64(Q, K, V, O, LSE, P, B, H, H, S_q, S_k, D_qk, D_v, scale, causal,
                             0, 0, 0, S_k, rows, n_rows, nthreads);
 }

@@ -458,6 +458,44 @@ def pin_ext_partition_merge(lib):
         assert np.all(o_m[empty] == 0.0)
 
 
+def pin_gqa_library(lib):
+    """Grouped K/V heads against the library routine's own grouped-head mode
+    (torch SDPA, enable_gqa): query head h attends with K/V head
+    h // (H / H_kv)."""
+    rng = np.random.default_rng(51)
+    for B, H, H_kv, S, D, causal in ((1, 6, 2, 9, 4, False), (2, 8, 2, 13, 8, True),
+                                     (1, 4, 1, 5, 3, False), (1, 6, 3, 11, 5, True)):
+        q = _randn(rng, B, H, S, D)
+        k = _randn(rng, B, H_kv, S, D)
+        v = _randn(rng, B, H_kv, S, D + 2)
+        o, lse = _ext(lib, q, k, v, 0.45, causal)
+        Q, K, V = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+        o_t = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=causal,
+                                                               scale=0.45, enable_gqa=True)
+        _close(o, o_t.numpy(), 1e-12, f"gqa H={H} H_kv={H_kv} causal={causal} O")
+
+
+def pin_gqa_head_map(lib):
+    """V constant per K/V head (head j holds j + 1): every output of query
+    head h is exactly h // (H / H_kv) + 1, whatever the scores; and a group's
+    query heads with equal Q rows produce equal results."""
+    rng = np.random.default_rng(52)
+    B, H, H_kv, S_q, S_k, D = 2, 12, 4, 7, 10, 5
+    g = H // H_kv
+    q = _randn(rng, B, H, S_q, D)
+    k = _randn(rng, B, H_kv, S_k, D)
+    v = np.broadcast_to(np.arange(1, H_kv + 1, dtype=np.float64)[None, :, None, None],
+                        (B, H_kv, S_k, 3)).copy()
+    o, _ = _ext(lib, q, k, v, 0.7, True, causal_offset=2)
+    for h in range(H):
+        assert np.all(np.abs(o[:, h] - (h // g + 1)) < 1e-13), f"head map: head {h}"
+    v = _randn(rng, B, H_kv, S_k, 3)
+    q[:, 1::g] = q[:, 0::g]       # second head of each group repeats the first's Q
+    o, lse = _ext(lib, q, k, v, 0.7, False)
+    _close(o[:, 1::g], o[:, 0::g], 0.0, "head map: equal heads O")
+    _close(lse[:, 1::g], lse[:, 0::g], 0.0, "head map: equal heads LSE")
+
+
 PINS = [
     pin_library_sdpa,
     pin_highprec_unshifted,
@@ -478,4 +516,6 @@ PINS = [
     pin_ext_brute_force,
     pin_ext_window_of_one,
     pin_ext_partition_merge,
+    pin_gqa_library,
+    pin_gqa_head_map,
 ]

@@ -36,8 +36,8 @@ MUTATIONS = [
     ("max seeded with 0", "double m = -INFINITY;", "double m = 0.0;"),
     ("wrong query row", "(slice * jb->S_q + i) * jb->D_qk",
      "(slice * jb->S_q + (i > 0 ? i - 1 : 0)) * jb->D_qk"),
-    ("V slice stride uses D_qk", "jb->V + slice * jb->S_k * jb->D_v",
-     "jb->V + slice * jb->S_k * jb->D_qk"),
+    ("V slice stride uses D_qk", "jb->V + kv_slice * jb->S_k * jb->D_v",
+     "jb->V + kv_slice * jb->S_k * jb->D_qk"),
     ("first key skipped", "for (int64_t j = lo; j < hi; ++j)\n        w[j]",
      "for (int64_t j = lo + 1; j < hi; ++j)\n        w[j]"),
     ("causal offset ignored", "hi = i + jb->coff + 1;", "hi = i + 1;"),
@@ -48,6 +48,9 @@ MUTATIONS = [
     ("key range start ignored", "int64_t lo = jb->kv_begin, hi", "int64_t lo = 0, hi"),
     ("empty row LSE zero", "jb->LSE[slice * jb->n_rows + out_row] = -INFINITY;",
      "jb->LSE[slice * jb->n_rows + out_row] = 0.0;"),
+    ("K/V head by modulo", "(slice % jb->H) / (jb->H / jb->H_kv)",
+     "(slice % jb->H) % jb->H_kv"),
+    ("K/V batch ignored", "(slice / jb->H) * jb->H_kv +", "0 * jb->H_kv +"),
 ]
 
 
