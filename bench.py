@@ -282,7 +282,8 @@ def main():
     else:   # splitkv: partial results over key chunks, then the merge
         mask = tsd.make_mask(w.S_k, w.causal_offset, w.window)
         n, split_len, _ = tsd.attn_splitkv_plan(w.B, w.H, w.S_q, w.S_k, w.D_qk, w.D_v,
-                                                w.causal, w.dtype, mask, w.n_splits)
+                                                w.causal, w.dtype, mask, w.n_splits,
+                                                H_kv=w.kv_heads)
         o_parts = torch.empty((n, w.B, w.H, w.S_q, w.D_v), dtype=torch.float32, device=dev)
         l_parts = torch.empty((n, w.B, w.H, w.S_q), dtype=torch.float32, device=dev)
         phases = [
@@ -345,8 +346,8 @@ def main():
         extra["merge_gbs"] = round(extra["merge_bytes_per_launch"] / (launch_ms[1] * 1e-3) / 1e9,
                                    1)
     if entry != "fwd":
-        extra.update(entry=entry, causal_offset=w.causal_offset, window=w.window,
-                     visible_pairs_per_slice=w.visible_pairs())
+        extra.update(entry=entry, H_kv=w.kv_heads, causal_offset=w.causal_offset,
+                     window=w.window, visible_pairs_per_slice=w.visible_pairs())
 
     result = {
         "metric": ("attention fwd TFLOP/s and % of MFMA peak (bf16 causal, S=16k, D=128)"

@@ -125,6 +125,15 @@ int attn_fwd_plan_block(const tsd_plan *plan, int64_t S_q, int64_t S_k,
  * of 8 (else TSD_ERR_UNSUPPORTED).  Buffer ownership, threading and
  * synchronisation are as for attn_fwd.
  *
+ * Grouped K/V heads (H_kv).  Q [B,H,S_q,D_qk], O [B,H,S_q,D_v] and LSE
+ * [B,H,S_q] keep H heads; K [B,H_kv,S_k,D_qk] and V [B,H_kv,S_k,D_v] hold
+ * H_kv heads, H a multiple of H_kv (else TSD_ERR_SHAPE), and query head h
+ * reads K/V head h / (H / H_kv) (VeriTile proof coverage, attention_score:
+ * program p of batch p / H reads K head (p mod H) / (H / H_KV)).  H_kv = H
+ * is the usual layout; H_kv = 1 shares one K/V head among all heads.  The
+ * H / H_kv query heads of a group are processed as one slice of their
+ * stacked rows, so each K/V tile is read once for the whole group.
+ *
  * Key visibility (tsd_mask).  Query row i of a slice sees exactly the keys
  *   j in [lo_i, hi_i),
  *   lo_i = max(kv_begin, i + causal_offset - window + 1)   (window > 0)
@@ -162,7 +171,7 @@ typedef struct tsd_mask {
  * plus the mask and fast-path conditions above.
  */
 int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
-                 int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                 int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                  int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
                  const tsd_mask *mask, void *stream);
 
@@ -182,7 +191,7 @@ int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LS
  */
 int attn_fwd_partial(const void *Q, const void *K, const void *V,
                      float *O_parts, float *LSE_parts,
-                     int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                     int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                      int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
                      const tsd_mask *mask, int64_t n_splits, int64_t split_len,
                      void *stream);
@@ -213,7 +222,7 @@ int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
  * length in keys and the workspace bytes attn_fwd_splitkv needs (0 when a
  * single chunk is used: then no workspace is touched).
  */
-int attn_splitkv_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+int attn_splitkv_plan(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                       int64_t D_qk, int64_t D_v, int causal, int dtype,
                       const tsd_mask *mask, int64_t n_splits,
                       int64_t *splits_out, int64_t *split_len_out,
@@ -230,7 +239,7 @@ int attn_splitkv_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
  * none.  Too small a workspace: TSD_ERR_SHAPE.
  */
 int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
-                     int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                     int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                      int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
                      const tsd_mask *mask, int64_t n_splits,
                      void *workspace, int64_t workspace_bytes, void *stream);

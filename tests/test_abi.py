@@ -224,17 +224,19 @@ def test_product_code_does_not_touch_the_oracle():
 MK = tsd.make_mask
 
 
-def ext(q=QA, k=KA, v=VA, o=OA, lse=LA, dtype=2, mask=None, **dims):
+def ext(q=QA, k=KA, v=VA, o=OA, lse=LA, dtype=2, mask=None, H_kv=None, **dims):
     d = dict(GOOD)
     d.update(dims)
-    return tsd.attn_fwd_ext_raw(q, k, v, o, lse, d["B"], d["H"], d["S_q"], d["S_k"],
+    return tsd.attn_fwd_ext_raw(q, k, v, o, lse, d["B"], d["H"],
+                                d["H"] if H_kv is None else H_kv, d["S_q"], d["S_k"],
                                 d["D_qk"], d["D_v"], 0.125, 1, dtype, mask)
 
 
-def part(op=OA, lp=LA, n=2, ln=64, mask=None, dtype=2, q=QA, **dims):
+def part(op=OA, lp=LA, n=2, ln=64, mask=None, dtype=2, q=QA, H_kv=None, **dims):
     d = dict(GOOD)
     d.update(dims)
-    return tsd.attn_fwd_partial_raw(q, KA, VA, op, lp, d["B"], d["H"], d["S_q"], d["S_k"],
+    return tsd.attn_fwd_partial_raw(q, KA, VA, op, lp, d["B"], d["H"],
+                                    d["H"] if H_kv is None else H_kv, d["S_q"], d["S_k"],
                                     d["D_qk"], d["D_v"], 0.125, 0, dtype, mask, n, ln)
 
 
@@ -268,6 +270,16 @@ def test_ext_alias(lib):
     # the chunked output spans n times the slice outputs: chunk 1 would reach LA
     o_bytes = 1 * 2 * 128 * 64 * 4
     assert part(op=LA - o_bytes, n=2) == 5
+
+
+def test_grouped_heads_rejected(lib):
+    for H_kv in (0, -1, 3):                   # H = 2: 3 does not divide it
+        assert ext(H_kv=H_kv) == 2
+        assert part(H_kv=H_kv) == 2
+    with pytest.raises(tsd.TsdError):
+        tsd.attn_splitkv_plan(1, 6, 64, 1000, 64, 64, False, "bf16", None, 0, H_kv=4)
+    # a group's rows form one slice: its 32-bit offsets bound H / H_kv * S_q
+    assert ext(H=64, H_kv=1, S_q=1 << 18) == 3
 
 
 def test_partial_bad_chunks(lib):
@@ -318,7 +330,7 @@ def test_splitkv_plan(lib):
 def test_splitkv_workspace_checks(lib):
     n, ln, ws = tsd.attn_splitkv_plan(1, 2, 128, 4096, 64, 64, False, "bf16", None, 4)
     assert n == 4 and ws > 0
-    args = (QA, KA, VA, OA, LA, 1, 2, 128, 4096, 64, 64, 0.125, 0, 2, None, 4)
+    args = (QA, KA, VA, OA, LA, 1, 2, 2, 128, 4096, 64, 64, 0.125, 0, 2, None, 4)
     assert tsd.attn_fwd_splitkv_raw(*args, None, ws) == 1          # no workspace
     assert tsd.attn_fwd_splitkv_raw(*args, 0x60000000, ws - 1) == 2  # too small
     assert tsd.attn_fwd_splitkv_raw(*args, 0x60000000 + 64, ws) == 3  # not 256-aligned

@@ -239,3 +239,69 @@ def test_splitkv_reuses_workspace():
     o_ref, lse_ref = ref_ext(q[:, :2, :50], k[:, :2, :3000], v[:, :2, :3000],
                              1 / math.sqrt(128), False)
     check(to_np(o2), to_np(l2), o_ref, lse_ref, "bf16", "splitkv reuse")
+
+
+# ------------------------------------------------------- grouped K/V heads
+GQA = [
+    # B, H, H_kv, S_q, S_k, D, causal, causal_offset, window
+    (1, 8, 2, 300, 700, 128, True, 400, 0),      # a workgroup's rows span two heads
+    (2, 6, 3, 129, 257, 64, False, 0, 0),
+    (1, 8, 1, 1, 3000, 128, True, 2999, 0),      # one K/V head, one query: decoding
+    (2, 32, 8, 1, 4096, 128, True, 4095, 0),
+    (1, 4, 2, 200, 600, 64, True, 400, 150),     # window
+    (1, 4, 4, 300, 300, 128, True, 0, 0),        # H_kv = H
+    (1, 16, 2, 40, 900, 128, True, 860, 64),     # 8 heads of 40 rows per slice
+]
+
+
+def gqa_id(c):
+    return "gqa_{}x{}kv{}_{}x{}_d{}_c{}_off{}_w{}".format(*(int(x) for x in c))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", GQA, ids=[gqa_id(c) for c in GQA])
+def test_gqa_ext(case, dtype):
+    B, H, H_kv, S_q, S_k, D, causal, coff, window = case
+    print(f"[case] {gqa_id(case)} {dtype}", flush=True)
+    scale = 1 / math.sqrt(D)
+    q, k, v = random_inputs((B, H, S_q, D), (B, H_kv, S_k, D), (B, H_kv, S_k, D), dtype,
+                            seed=5000 + H * 7 + H_kv + S_q)
+    o, lse = tsd.attn_fwd_ext(*gpu(q, k, v), scale=scale, causal=causal, causal_offset=coff,
+                              window=window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_ext(q, k, v, scale, causal, coff, window)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"{gqa_id(case)} {dtype}")
+
+
+@pytest.mark.parametrize("case", [(4, 32, 8, 1, 16384, 128, True, 16383, 0, 0),
+                                  (1, 8, 2, 64, 5000, 128, True, 4936, 0, 5),
+                                  (2, 4, 1, 3, 3000, 64, False, 0, 0, 3)],
+                         ids=["decode_auto", "chunk_n5", "mqa_n3"])
+def test_gqa_splitkv(case):
+    B, H, H_kv, S_q, S_k, D, causal, coff, window, n = case
+    print(f"[case] gqa splitkv {case}", flush=True)
+    scale = 1 / math.sqrt(D)
+    q, k, v = random_inputs((B, H, S_q, D), (B, H_kv, S_k, D), (B, H_kv, S_k, D), "bf16",
+                            seed=6000 + S_k)
+    plan = tsd.attn_splitkv_plan(B, H, S_q, S_k, D, D, causal, "bf16",
+                                 tsd.make_mask(S_k, coff, window), n, H_kv=H_kv)
+    print(f"[plan] chunks={plan[0]} keys/chunk={plan[1]} workspace={plan[2]}", flush=True)
+    o, lse = tsd.attn_fwd_splitkv(*gpu(q, k, v), scale=scale, causal=causal,
+                                  causal_offset=coff, window=window, n_splits=n)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_ext(q, k, v, scale, causal, coff, window)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, "bf16", f"gqa splitkv {case}")
+
+
+def test_gqa_partial():
+    B, H, H_kv, S_q, S_k, D, n, ln = 1, 6, 2, 50, 1000, 64, 4, 256
+    q, k, v = random_inputs((B, H, S_q, D), (B, H_kv, S_k, D), (B, H_kv, S_k, D), "bf16",
+                            seed=61)
+    op, lp = tsd.attn_fwd_partial(*gpu(q, k, v), n, ln, scale=0.125, causal=True,
+                                  causal_offset=S_k - S_q)
+    torch.cuda.synchronize()
+    op, lp = to_np(op), to_np(lp)
+    for s in range(n):
+        o_ref, lse_ref = ref_ext(q, k, v, 0.125, True, S_k - S_q, 0, s * ln,
+                                 min(S_k, (s + 1) * ln))
+        check(op[s], lp[s], o_ref, lse_ref, "bf16", f"gqa partial chunk {s}")

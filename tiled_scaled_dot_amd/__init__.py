@@ -107,20 +107,20 @@ def library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     mp, f, ci = ctypes.POINTER(TsdMask), ctypes.c_float, ctypes.c_int
-    lib.attn_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f, ci, ci,
-                                 mp, vp]
+    lib.attn_fwd_ext.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f, ci,
+                                 ci, mp, vp]
     lib.attn_fwd_ext.restype = ci
-    lib.attn_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f, ci,
-                                     ci, mp, i64, i64, vp]
+    lib.attn_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f,
+                                     ci, ci, mp, i64, i64, vp]
     lib.attn_fwd_partial.restype = ci
     lib.attn_merge.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, ci, vp]
     lib.attn_merge.restype = ci
-    lib.attn_splitkv_plan.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, mp, i64,
+    lib.attn_splitkv_plan.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci, ci, mp, i64,
                                       ctypes.POINTER(i64), ctypes.POINTER(i64),
                                       ctypes.POINTER(i64)]
     lib.attn_splitkv_plan.restype = ci
-    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f, ci,
-                                     ci, mp, i64, vp, i64, vp]
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f,
+                                     ci, ci, mp, i64, vp, i64, vp]
     lib.attn_fwd_splitkv.restype = ci
     _lib = lib
     return lib
@@ -167,18 +167,20 @@ def _mask_ref(mask):
     return None if mask is None else ctypes.byref(mask)
 
 
-def attn_fwd_ext_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk, D_v, scale,
-                     causal, dtype, mask=None, stream=None) -> int:
-    return library().attn_fwd_ext(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk,
-                                  D_v, float(scale), int(bool(causal)), _code(dtype),
+def attn_fwd_ext_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, H_kv, S_q, S_k, D_qk, D_v,
+                     scale, causal, dtype, mask=None, stream=None) -> int:
+    return library().attn_fwd_ext(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, H_kv, S_q, S_k,
+                                  D_qk, D_v, float(scale), int(bool(causal)), _code(dtype),
                                   _mask_ref(mask), stream)
 
 
-def attn_fwd_partial_raw(q_ptr, k_ptr, v_ptr, op_ptr, lp_ptr, B, H, S_q, S_k, D_qk, D_v,
-                         scale, causal, dtype, mask, n_splits, split_len, stream=None) -> int:
-    return library().attn_fwd_partial(q_ptr, k_ptr, v_ptr, op_ptr, lp_ptr, B, H, S_q, S_k,
-                                      D_qk, D_v, float(scale), int(bool(causal)), _code(dtype),
-                                      _mask_ref(mask), n_splits, split_len, stream)
+def attn_fwd_partial_raw(q_ptr, k_ptr, v_ptr, op_ptr, lp_ptr, B, H, H_kv, S_q, S_k, D_qk,
+                         D_v, scale, causal, dtype, mask, n_splits, split_len,
+                         stream=None) -> int:
+    return library().attn_fwd_partial(q_ptr, k_ptr, v_ptr, op_ptr, lp_ptr, B, H, H_kv, S_q,
+                                      S_k, D_qk, D_v, float(scale), int(bool(causal)),
+                                      _code(dtype), _mask_ref(mask), n_splits, split_len,
+                                      stream)
 
 
 def attn_merge_raw(op_ptr, lp_ptr, n_parts, B, H, S_q, D_v, o_ptr, lse_ptr, dtype,
@@ -187,26 +189,30 @@ def attn_merge_raw(op_ptr, lp_ptr, n_parts, B, H, S_q, D_v, o_ptr, lse_ptr, dtyp
                                 _code(dtype), stream)
 
 
-def attn_fwd_splitkv_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k, D_qk, D_v,
-                         scale, causal, dtype, mask, n_splits, ws_ptr, ws_bytes,
+def attn_fwd_splitkv_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, H_kv, S_q, S_k, D_qk,
+                         D_v, scale, causal, dtype, mask, n_splits, ws_ptr, ws_bytes,
                          stream=None) -> int:
-    return library().attn_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S_q, S_k,
-                                      D_qk, D_v, float(scale), int(bool(causal)), _code(dtype),
-                                      _mask_ref(mask), n_splits, ws_ptr, ws_bytes, stream)
+    return library().attn_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, H_kv, S_q,
+                                      S_k, D_qk, D_v, float(scale), int(bool(causal)),
+                                      _code(dtype), _mask_ref(mask), n_splits, ws_ptr,
+                                      ws_bytes, stream)
 
 
 def attn_splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal=False, dtype="bf16", mask=None,
-                      n_splits=0):
+                      n_splits=0, H_kv=None):
     """(chunks, keys per chunk, workspace bytes) attn_fwd_splitkv would use."""
     n, ln, ws = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    _check(library().attn_splitkv_plan(B, H, S_q, S_k, D_qk, D_v, int(bool(causal)),
-                                       _code(dtype), _mask_ref(mask), n_splits,
-                                       ctypes.byref(n), ctypes.byref(ln), ctypes.byref(ws)))
+    _check(library().attn_splitkv_plan(B, H, H if H_kv is None else H_kv, S_q, S_k, D_qk, D_v,
+                                       int(bool(causal)), _code(dtype), _mask_ref(mask),
+                                       n_splits, ctypes.byref(n), ctypes.byref(ln),
+                                       ctypes.byref(ws)))
     return n.value, ln.value, ws.value
 
 
-def _qkv(q, k, v):
-    """Validate q, k, v tensors; returns (dtype code, B, H, S_q, S_k, D_qk, D_v)."""
+def _qkv(q, k, v, grouped=False):
+    """Validate q, k, v tensors; returns (dtype code, B, H, S_q, S_k, D_qk, D_v)
+    (with H_kv appended when ``grouped``: k and v may then hold fewer heads,
+    a divisor of q's)."""
     import torch
 
     codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
@@ -221,9 +227,13 @@ def _qkv(q, k, v):
             raise ValueError(f"{name} must be contiguous")
     B, H, S_q, D_qk = q.shape
     S_k, D_v = k.shape[2], v.shape[3]
-    if tuple(k.shape) != (B, H, S_k, D_qk) or tuple(v.shape) != (B, H, S_k, D_v):
+    H_kv = k.shape[1] if grouped else H
+    if (tuple(k.shape) != (B, H_kv, S_k, D_qk) or tuple(v.shape) != (B, H_kv, S_k, D_v)
+            or H % H_kv != 0):
         raise ValueError(f"inconsistent shapes q{tuple(q.shape)} k{tuple(k.shape)} "
                          f"v{tuple(v.shape)}")
+    if grouped:
+        return codes[q.dtype], B, H, H_kv, S_q, S_k, D_qk, D_v
     return codes[q.dtype], B, H, S_q, S_k, D_qk, D_v
 
 
@@ -250,18 +260,20 @@ def _stream(stream, device):
 def attn_fwd_ext(q, k, v, scale=None, causal=False, causal_offset=0, window=0, kv_begin=0,
                  kv_end=None, out=None, lse=None, stream=None):
     """attn_fwd restricted per row to the keys of the mask (see TsdMask);
-    rows that see no key get O = 0 and LSE = -inf.  16-bit inputs only."""
+    rows that see no key get O = 0 and LSE = -inf.  16-bit inputs only.  k
+    and v may hold H_kv heads (a divisor of q's H): head h reads K/V head
+    h // (H // H_kv)."""
     import torch
 
-    code, B, H, S_q, S_k, D_qk, D_v = _qkv(q, k, v)
+    code, B, H, H_kv, S_q, S_k, D_qk, D_v = _qkv(q, k, v, grouped=True)
     if scale is None:
         scale = 1.0 / math.sqrt(D_qk)
     out = _buffer(out, (B, H, S_q, D_v), q.dtype, q, "out")
     lse = _buffer(lse, (B, H, S_q), torch.float32, q, "lse")
     mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
     _check(attn_fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal, code,
-                            mask, _stream(stream, q.device)))
+                            lse.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
+                            code, mask, _stream(stream, q.device)))
     return out, lse
 
 
@@ -273,15 +285,16 @@ def attn_fwd_partial(q, k, v, n_splits, split_len, scale=None, causal=False, cau
     onwards (split_len keys, cut to the range)."""
     import torch
 
-    code, B, H, S_q, S_k, D_qk, D_v = _qkv(q, k, v)
+    code, B, H, H_kv, S_q, S_k, D_qk, D_v = _qkv(q, k, v, grouped=True)
     if scale is None:
         scale = 1.0 / math.sqrt(D_qk)
     o_parts = _buffer(o_parts, (n_splits, B, H, S_q, D_v), torch.float32, q, "o_parts")
     lse_parts = _buffer(lse_parts, (n_splits, B, H, S_q), torch.float32, q, "lse_parts")
     mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
     _check(attn_fwd_partial_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts.data_ptr(),
-                                lse_parts.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal,
-                                code, mask, n_splits, split_len, _stream(stream, q.device)))
+                                lse_parts.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale,
+                                causal, code, mask, n_splits, split_len,
+                                _stream(stream, q.device)))
     return o_parts, lse_parts
 
 
@@ -315,20 +328,22 @@ def attn_fwd_splitkv(q, k, v, scale=None, causal=False, causal_offset=0, window=
     planned size (allocated here when None)."""
     import torch
 
-    code, B, H, S_q, S_k, D_qk, D_v = _qkv(q, k, v)
+    code, B, H, H_kv, S_q, S_k, D_qk, D_v = _qkv(q, k, v, grouped=True)
     if scale is None:
         scale = 1.0 / math.sqrt(D_qk)
     out = _buffer(out, (B, H, S_q, D_v), q.dtype, q, "out")
     lse = _buffer(lse, (B, H, S_q), torch.float32, q, "lse")
     mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
-    _, _, ws = attn_splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal, code, mask, n_splits)
+    _, _, ws = attn_splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal, code, mask, n_splits,
+                                 H_kv=H_kv)
     if workspace is None and ws > 0:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(attn_fwd_splitkv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                lse.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal, code,
-                                mask, n_splits, ws_ptr, ws_bytes, _stream(stream, q.device)))
+                                lse.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
+                                code, mask, n_splits, ws_ptr, ws_bytes,
+                                _stream(stream, q.device)))
     return out, lse
 
 

@@ -124,6 +124,7 @@ tsd::KernelArgs base_args(const void *Q, const void *K, const void *V, void *O, 
     a.split_len = (int32_t)S_k;
     a.part_o_stride = 0;
     a.part_lse_stride = 0;
+    a.q_per_head = (int32_t)S_q;
     return a;
 }
 
@@ -145,18 +146,30 @@ int check_mask(const tsd_mask *mask, int64_t S_k, tsd_mask *out)
     return TSD_OK;
 }
 
+// Sizes of an extended call.  Q, O and LSE have H heads, K and V H_kv;
+// the kernels see one slice per K/V head whose rows are the query rows of
+// its H / H_kv query heads (contiguous in Q, O and LSE), position = row
+// modulo S_q.
+struct ExtShape {
+    int64_t B, H, H_kv, S_q, S_k, D_qk, D_v;
+    int64_t group() const { return H / H_kv; }
+    int64_t rows() const { return group() * S_q; }   // rows per kernel slice
+};
+
 // Checks shared by the extended entry points (which run on the LDS-direct
 // kernel only): 16-bit dtype, 16-byte aligned Q/K/V, widths a multiple of 8.
-int check_ext_inputs(const void *Q, const void *K, const void *V, int64_t B, int64_t H,
-                     int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v, float scale,
-                     int dtype)
+int check_ext_inputs(const void *Q, const void *K, const void *V, const ExtShape &es,
+                     float scale, int dtype)
 {
     if (!Q || !K || !V) return TSD_ERR_NULL;
-    const int st = check_shape(B, H, S_q, S_k, D_qk, D_v, dtype);
+    if (es.B < 1 || es.H < 1 || es.H_kv < 1 || es.S_q < 1 || es.H % es.H_kv != 0)
+        return TSD_ERR_SHAPE;
+    if (es.rows() > INT32_MAX) return TSD_ERR_UNSUPPORTED;
+    const int st = check_shape(es.B, es.H_kv, es.rows(), es.S_k, es.D_qk, es.D_v, dtype);
     if (st != TSD_OK) return st;
     if (!std::isfinite(scale)) return TSD_ERR_SCALE;
     if (dtype == TSD_F32) return TSD_ERR_UNSUPPORTED;
-    if (!vector_dims_ok(dtype, D_qk, D_v)) return TSD_ERR_UNSUPPORTED;
+    if (!vector_dims_ok(dtype, es.D_qk, es.D_v)) return TSD_ERR_UNSUPPORTED;
     for (uintptr_t p : {(uintptr_t)Q, (uintptr_t)K, (uintptr_t)V})
         if (p % 16 != 0) return TSD_ERR_UNSUPPORTED;
     return TSD_OK;
@@ -166,11 +179,12 @@ int check_ext_inputs(const void *Q, const void *K, const void *V, int64_t B, int
 struct InputBytes {
     uint64_t q, k, v;
 };
-InputBytes input_bytes(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk,
-                       int64_t D_v, int dtype)
+InputBytes input_bytes(const ExtShape &es, int dtype)
 {
-    const uint64_t elt = (uint64_t)elt_bytes(dtype), BH = (uint64_t)B * (uint64_t)H;
-    return InputBytes{BH * S_q * D_qk * elt, BH * S_k * D_qk * elt, BH * S_k * D_v * elt};
+    const uint64_t elt = (uint64_t)elt_bytes(dtype);
+    const uint64_t BH = (uint64_t)es.B * es.H, BHk = (uint64_t)es.B * es.H_kv;
+    return InputBytes{BH * es.S_q * es.D_qk * elt, BHk * es.S_k * es.D_qk * elt,
+                      BHk * es.S_k * es.D_v * elt};
 }
 
 bool overlaps_inputs(const void *p, uint64_t n, const void *Q, const void *K, const void *V,
@@ -182,15 +196,17 @@ bool overlaps_inputs(const void *p, uint64_t n, const void *Q, const void *K, co
 // Launch the extended kernel over `splits` chunks of `split_len` keys
 // starting at mask.kv_begin (splits = 1: the whole range).  out_f32: O and
 // LSE are the chunked f32 partial buffers.
-int launch_ext(const void *Q, const void *K, const void *V, void *O, float *LSE, int64_t B,
-               int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v, float scale,
-               int causal, int dtype, const tsd_mask &mk, int64_t splits, int64_t split_len,
-               bool out_f32, hipStream_t stream)
+int launch_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
+               const ExtShape &es, float scale, int causal, int dtype, const tsd_mask &mk,
+               int64_t splits, int64_t split_len, bool out_f32, hipStream_t stream)
 {
+    const int64_t S_q = es.rows(), D_v = es.D_v;   // the kernel's view
     tsd_plan plan;
-    fill_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, true, &plan);
+    fill_plan(es.B, es.H_kv, S_q, es.S_k, es.D_qk, D_v, causal, dtype, true, &plan);
     if (plan.grid > INT32_MAX / splits) return TSD_ERR_UNSUPPORTED;
-    tsd::KernelArgs a = base_args(Q, K, V, O, LSE, S_q, S_k, D_qk, D_v, scale, dtype, true, plan);
+    tsd::KernelArgs a =
+        base_args(Q, K, V, O, LSE, S_q, es.S_k, es.D_qk, D_v, scale, dtype, true, plan);
+    a.q_per_head = (int32_t)es.S_q;
     a.kv_begin = (int32_t)mk.kv_begin;
     a.kv_end = (int32_t)mk.kv_end;
     a.coff = (int32_t)mk.causal_offset;
@@ -201,7 +217,7 @@ int launch_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
         a.part_o_stride = plan.slices * S_q * D_v;
         a.part_lse_stride = plan.slices * S_q;
     }
-    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, true);
+    const tsd::TileConfig cfg = tsd::tile_config(dtype, es.D_qk, D_v, true);
     const hipError_t err = tsd::launch_attn_ext(cfg, dtype, causal != 0, out_f32,
                                                 plan.grid * splits, a, stream);
     return err == hipSuccess ? TSD_OK : TSD_ERR_HIP;
@@ -301,33 +317,35 @@ extern "C" int attn_fwd(const void *Q, const void *K, const void *V, void *O, fl
 }
 
 extern "C" int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
-                            int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk,
-                            int64_t D_v, float scale, int causal, int dtype,
+                            int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
+                            int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
                             const tsd_mask *mask, void *stream)
 {
-    int st = check_ext_inputs(Q, K, V, B, H, S_q, S_k, D_qk, D_v, scale, dtype);
+    const ExtShape es{B, H, H_kv, S_q, S_k, D_qk, D_v};
+    int st = check_ext_inputs(Q, K, V, es, scale, dtype);
     if (st != TSD_OK) return st;
     if (!O) return TSD_ERR_NULL;
     tsd_mask mk;
     if ((st = check_mask(mask, S_k, &mk)) != TSD_OK) return st;
     if ((uintptr_t)O % 16 != 0 || (uintptr_t)LSE % 4 != 0) return TSD_ERR_UNSUPPORTED;
-    const InputBytes ib = input_bytes(B, H, S_q, S_k, D_qk, D_v, dtype);
+    const InputBytes ib = input_bytes(es, dtype);
     const uint64_t rows = (uint64_t)B * H * S_q;
     const uint64_t o_bytes = rows * D_v * 2, l_bytes = LSE ? rows * 4 : 0;
     if (overlaps_inputs(O, o_bytes, Q, K, V, ib) || overlaps_inputs(LSE, l_bytes, Q, K, V, ib) ||
         overlap(LSE, l_bytes, O, o_bytes))
         return TSD_ERR_ALIAS;
-    return launch_ext(Q, K, V, O, LSE, B, H, S_q, S_k, D_qk, D_v, scale, causal, dtype, mk, 1,
+    return launch_ext(Q, K, V, O, LSE, es, scale, causal, dtype, mk, 1,
                       mk.kv_end - mk.kv_begin, false, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int attn_fwd_partial(const void *Q, const void *K, const void *V, float *O_parts,
-                                float *LSE_parts, int64_t B, int64_t H, int64_t S_q,
-                                int64_t S_k, int64_t D_qk, int64_t D_v, float scale,
-                                int causal, int dtype, const tsd_mask *mask, int64_t n_splits,
-                                int64_t split_len, void *stream)
+                                float *LSE_parts, int64_t B, int64_t H, int64_t H_kv,
+                                int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
+                                float scale, int causal, int dtype, const tsd_mask *mask,
+                                int64_t n_splits, int64_t split_len, void *stream)
 {
-    int st = check_ext_inputs(Q, K, V, B, H, S_q, S_k, D_qk, D_v, scale, dtype);
+    const ExtShape es{B, H, H_kv, S_q, S_k, D_qk, D_v};
+    int st = check_ext_inputs(Q, K, V, es, scale, dtype);
     if (st != TSD_OK) return st;
     if (!O_parts || !LSE_parts) return TSD_ERR_NULL;
     tsd_mask mk;
@@ -336,10 +354,10 @@ extern "C" int attn_fwd_partial(const void *Q, const void *K, const void *V, flo
     // chunk bounds kv_begin + s * split_len stay inside int32
     if (split_len > INT32_MAX || n_splits > (INT32_MAX - mk.kv_begin) / split_len)
         return TSD_ERR_UNSUPPORTED;
-    if (S_q > kMaxSliceBytes / (D_v * 4)) return TSD_ERR_UNSUPPORTED;   // f32 slice of O
+    if (es.rows() > kMaxSliceBytes / (D_v * 4)) return TSD_ERR_UNSUPPORTED;   // f32 slice of O
     if ((uintptr_t)O_parts % 16 != 0 || (uintptr_t)LSE_parts % 4 != 0)
         return TSD_ERR_UNSUPPORTED;
-    const InputBytes ib = input_bytes(B, H, S_q, S_k, D_qk, D_v, dtype);
+    const InputBytes ib = input_bytes(es, dtype);
     const uint64_t rows = (uint64_t)B * H * S_q;
     const uint64_t o_bytes = (uint64_t)n_splits * rows * D_v * 4;
     const uint64_t l_bytes = (uint64_t)n_splits * rows * 4;
@@ -347,8 +365,8 @@ extern "C" int attn_fwd_partial(const void *Q, const void *K, const void *V, flo
         overlaps_inputs(LSE_parts, l_bytes, Q, K, V, ib) ||
         overlap(LSE_parts, l_bytes, O_parts, o_bytes))
         return TSD_ERR_ALIAS;
-    return launch_ext(Q, K, V, O_parts, LSE_parts, B, H, S_q, S_k, D_qk, D_v, scale, causal,
-                      dtype, mk, n_splits, split_len, true, reinterpret_cast<hipStream_t>(stream));
+    return launch_ext(Q, K, V, O_parts, LSE_parts, es, scale, causal, dtype, mk, n_splits,
+                      split_len, true, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
@@ -397,12 +415,11 @@ namespace {
 // then (at a 256-byte boundary) the partial LSE.
 int64_t round256(int64_t x) { return (x + 255) / 256 * 256; }
 
-int splitkv_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
-                 int causal, int dtype, const tsd_mask &mk, int64_t n_splits,
-                 int64_t *splits_out, int64_t *split_len_out, int64_t *ws_out)
+int splitkv_plan(const ExtShape &es, int causal, int dtype, const tsd_mask &mk,
+                 int64_t n_splits, int64_t *splits_out, int64_t *split_len_out, int64_t *ws_out)
 {
     tsd_plan plan;
-    fill_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, true, &plan);
+    fill_plan(es.B, es.H_kv, es.rows(), es.S_k, es.D_qk, es.D_v, causal, dtype, true, &plan);
     const int64_t keys = mk.kv_end - mk.kv_begin;
     int64_t n = n_splits > 0 ? n_splits : auto_splits(plan, keys);
     if (n > kMaxSplits) return TSD_ERR_UNSUPPORTED;
@@ -411,54 +428,57 @@ int splitkv_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, i
     len = (len + 63) / 64 * 64;
     if (keys > 0) n = (keys + len - 1) / len;
     if (n > (INT32_MAX - mk.kv_begin) / len) return TSD_ERR_UNSUPPORTED;
-    if (n > 1 && S_q > kMaxSliceBytes / (D_v * 4)) return TSD_ERR_UNSUPPORTED;
-    const int64_t rows = B * H * S_q;
+    if (n > 1 && es.rows() > kMaxSliceBytes / (es.D_v * 4)) return TSD_ERR_UNSUPPORTED;
+    const int64_t rows = es.B * es.H * es.S_q;
     *splits_out = n;
     *split_len_out = len;
-    *ws_out = n > 1 ? round256(n * rows * D_v * 4) + round256(n * rows * 4) : 0;
+    *ws_out = n > 1 ? round256(n * rows * es.D_v * 4) + round256(n * rows * 4) : 0;
     return TSD_OK;
 }
 
 }  // namespace
 
-extern "C" int attn_splitkv_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk,
-                                 int64_t D_v, int causal, int dtype, const tsd_mask *mask,
-                                 int64_t n_splits, int64_t *splits_out, int64_t *split_len_out,
-                                 int64_t *workspace_bytes)
+extern "C" int attn_splitkv_plan(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
+                                 int64_t D_qk, int64_t D_v, int causal, int dtype,
+                                 const tsd_mask *mask, int64_t n_splits, int64_t *splits_out,
+                                 int64_t *split_len_out, int64_t *workspace_bytes)
 {
     if (!splits_out || !split_len_out || !workspace_bytes) return TSD_ERR_NULL;
-    int st = check_shape(B, H, S_q, S_k, D_qk, D_v, dtype);
+    const ExtShape es{B, H, H_kv, S_q, S_k, D_qk, D_v};
+    if (B < 1 || H < 1 || H_kv < 1 || S_q < 1 || H % H_kv != 0) return TSD_ERR_SHAPE;
+    if (es.rows() > INT32_MAX) return TSD_ERR_UNSUPPORTED;
+    int st = check_shape(B, H_kv, es.rows(), S_k, D_qk, D_v, dtype);
     if (st != TSD_OK) return st;
     if (dtype == TSD_F32 || !vector_dims_ok(dtype, D_qk, D_v)) return TSD_ERR_UNSUPPORTED;
     tsd_mask mk;
     if ((st = check_mask(mask, S_k, &mk)) != TSD_OK) return st;
-    return splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, mk, n_splits, splits_out,
-                        split_len_out, workspace_bytes);
+    return splitkv_plan(es, causal, dtype, mk, n_splits, splits_out, split_len_out,
+                        workspace_bytes);
 }
 
 extern "C" int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O,
-                                float *LSE, int64_t B, int64_t H, int64_t S_q, int64_t S_k,
-                                int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
-                                const tsd_mask *mask, int64_t n_splits, void *workspace,
-                                int64_t workspace_bytes, void *stream)
+                                float *LSE, int64_t B, int64_t H, int64_t H_kv, int64_t S_q,
+                                int64_t S_k, int64_t D_qk, int64_t D_v, float scale,
+                                int causal, int dtype, const tsd_mask *mask, int64_t n_splits,
+                                void *workspace, int64_t workspace_bytes, void *stream)
 {
-    int st = check_ext_inputs(Q, K, V, B, H, S_q, S_k, D_qk, D_v, scale, dtype);
+    const ExtShape es{B, H, H_kv, S_q, S_k, D_qk, D_v};
+    int st = check_ext_inputs(Q, K, V, es, scale, dtype);
     if (st != TSD_OK) return st;
     if (!O) return TSD_ERR_NULL;
     tsd_mask mk;
     if ((st = check_mask(mask, S_k, &mk)) != TSD_OK) return st;
     int64_t n = 0, len = 0, ws = 0;
-    if ((st = splitkv_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, mk, n_splits, &n, &len,
-                           &ws)) != TSD_OK)
+    if ((st = splitkv_plan(es, causal, dtype, mk, n_splits, &n, &len, &ws)) != TSD_OK)
         return st;
     if (n == 1)
-        return attn_fwd_ext(Q, K, V, O, LSE, B, H, S_q, S_k, D_qk, D_v, scale, causal, dtype,
-                            &mk, stream);
+        return attn_fwd_ext(Q, K, V, O, LSE, B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
+                            dtype, &mk, stream);
     if (!workspace) return TSD_ERR_NULL;
     if (workspace_bytes < ws) return TSD_ERR_SHAPE;
     if ((uintptr_t)workspace % 256 != 0) return TSD_ERR_UNSUPPORTED;
     if ((uintptr_t)O % 16 != 0 || (uintptr_t)LSE % 4 != 0) return TSD_ERR_UNSUPPORTED;
-    const InputBytes ib = input_bytes(B, H, S_q, S_k, D_qk, D_v, dtype);
+    const InputBytes ib = input_bytes(es, dtype);
     const uint64_t rows = (uint64_t)B * H * S_q;
     const uint64_t o_bytes = rows * D_v * 2, l_bytes = LSE ? rows * 4 : 0;
     if (overlaps_inputs(O, o_bytes, Q, K, V, ib) || overlaps_inputs(LSE, l_bytes, Q, K, V, ib) ||
@@ -469,8 +489,7 @@ extern "C" int attn_fwd_splitkv(const void *Q, const void *K, const void *V, voi
     float *l_parts = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) +
                                                round256((int64_t)(n * rows * D_v * 4)));
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    st = launch_ext(Q, K, V, o_parts, l_parts, B, H, S_q, S_k, D_qk, D_v, scale, causal, dtype,
-                    mk, n, len, true, s);
+    st = launch_ext(Q, K, V, o_parts, l_parts, es, scale, causal, dtype, mk, n, len, true, s);
     if (st != TSD_OK) return st;
     return attn_merge(o_parts, l_parts, n, B, H, S_q, D_v, O, LSE, dtype, stream);
 }

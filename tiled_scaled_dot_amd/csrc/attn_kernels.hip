@@ -903,8 +903,8 @@ attn_fwd_fast16(KernelArgs p)
     // key tiles of this workgroup: t_first .. t_first + ntiles - 1
     int t_first = 0, ntiles;
     if constexpr (EXT) {
-        const KeyRange kr = wg_key_range(q0, min(q0 + T::BM, p.S_q), klo, khi, CAUSAL, p.coff,
-                                         p.window);
+        const PosRange pr = row_positions(q0, min(q0 + T::BM, p.S_q), p.q_per_head);
+        const KeyRange kr = wg_key_range(pr.lo, pr.hi + 1, klo, khi, CAUSAL, p.coff, p.window);
         t_first = kr.key_lo / BN;
         ntiles = kr.key_hi > kr.key_lo ? (kr.key_hi + BN - 1) / BN - t_first : 0;
     } else {
@@ -1105,16 +1105,19 @@ attn_fwd_fast16(KernelArgs p)
 
     // Visible keys of this lane, [lo_i, hi_i), and of the wave: a tile needs
     // no mask when it lies inside every row's range, and the wave is idle
-    // on a tile outside every row's range.
+    // on a tile outside every row's range.  Ranges follow the query
+    // position, the row modulo the positions per head.
     int lo_i = 0, hi_i = 0, wave_lo_min = 0, wave_lo_max = 0, wave_hi_min = 0, wave_hi_max = 0;
     if constexpr (EXT) {
         const bool win = p.window > 0;
-        lo_i = win ? max(klo, qi + p.coff - p.window + 1) : klo;
-        hi_i = CAUSAL ? min(khi, qi + p.coff + 1) : khi;
-        wave_lo_min = win ? max(klo, qw + p.coff - p.window + 1) : klo;
-        wave_lo_max = win ? max(klo, qw + 31 + p.coff - p.window + 1) : klo;
-        wave_hi_min = CAUSAL ? min(khi, qw + p.coff + 1) : khi;
-        wave_hi_max = CAUSAL ? min(khi, qw + 31 + p.coff + 1) : khi;
+        const int pi = qi % p.q_per_head;
+        lo_i = win ? max(klo, pi + p.coff - p.window + 1) : klo;
+        hi_i = CAUSAL ? min(khi, pi + p.coff + 1) : khi;
+        const PosRange pw = row_positions(qw, min(qw + 32, p.S_q), p.q_per_head);
+        wave_lo_min = win ? max(klo, pw.lo + p.coff - p.window + 1) : klo;
+        wave_lo_max = win ? max(klo, pw.hi + p.coff - p.window + 1) : klo;
+        wave_hi_min = CAUSAL ? min(khi, pw.lo + p.coff + 1) : khi;
+        wave_hi_max = CAUSAL ? min(khi, pw.hi + p.coff + 1) : khi;
         if (qw >= p.S_q) wave_hi_max = -1;   // no row of the wave exists: idle throughout
     }
 

@@ -35,10 +35,13 @@ struct KernelArgs {
     int32_t split_len;          // ... of split_len keys (a multiple of 64)
     int64_t part_o_stride;      // elements between consecutive chunks' O (f32 output)
     int64_t part_lse_stride;    // elements between consecutive chunks' LSE
+    int32_t q_per_head;         // row r of a slice is query position r % q_per_head (grouped
+                                // heads: a slice holds the rows of every query head that
+                                // shares its K/V head); S_q when each slice is one head
 };
 
-// Keys a workgroup of query rows [q0, q_end) sees inside the key range
-// [klo, khi): row i sees [max(klo, i + coff - window + 1) (window > 0),
+// Keys a workgroup of query positions [q0, q_end) sees inside the key range
+// [klo, khi): position i sees [max(klo, i + coff - window + 1) (window > 0),
 // min(khi, i + coff + 1) (causal)); the workgroup's span is the union,
 // [key_lo, key_hi) (empty when key_hi <= key_lo).
 struct KeyRange {
@@ -53,6 +56,19 @@ __host__ __device__ inline KeyRange wg_key_range(int32_t q0, int32_t q_end, int3
     if (causal && (int64_t)q_end - 1 + coff + 1 < hi) hi = (int64_t)q_end - 1 + coff + 1;
     if (hi < lo) hi = lo;
     return KeyRange{(int32_t)lo, (int32_t)hi};
+}
+
+// Query positions (inclusive) of rows [r0, r1) of a slice whose rows are
+// heads x positions, qph positions per head: where the rows run into the
+// next head the range is every position.
+struct PosRange {
+    int32_t lo, hi;
+};
+__host__ __device__ inline PosRange row_positions(int32_t r0, int32_t r1, int32_t qph)
+{
+    const int32_t p0 = r0 % qph, p1 = (r1 - 1) % qph;
+    if (r1 - r0 >= qph || p1 < p0) return PosRange{0, qph - 1};
+    return PosRange{p0, p1};
 }
 
 // Workgroup index -> (query block, slice).

@@ -123,11 +123,25 @@ class ExtWorkload(Workload):
     [max(0, i + causal_offset - window + 1) if window else 0,
      min(S_k, i + causal_offset + 1) if causal else S_k).
     entry: "ext" (attn_fwd_ext, one launch) or "splitkv" (attn_fwd_partial
-    over key chunks, then attn_merge; n_splits 0 = the library's choice)."""
+    over key chunks, then attn_merge; n_splits 0 = the library's choice).
+    H_kv: K/V heads (0 = H); query head h reads K/V head h // (H // H_kv)."""
     causal_offset: int = 0
     window: int = 0
     entry: str = "ext"
     n_splits: int = 0
+    H_kv: int = 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
+
+    @property
+    def shape_k(self):
+        return (self.B, self.kv_heads, self.S_k, self.D_qk)
+
+    @property
+    def shape_v(self):
+        return (self.B, self.kv_heads, self.S_k, self.D_v)
 
     def row_ranges(self):
         import numpy as np
@@ -155,24 +169,27 @@ class ExtWorkload(Workload):
         return int(hi[live].max() - lo[live].min()) if live.any() else 0
 
     def min_bytes(self) -> int:
-        """Q, the keys and values some row sees, O (storage dtype) and LSE."""
+        """Q, the keys and values some row sees (once per K/V head), O
+        (storage dtype) and LSE."""
         elt = DTYPES[self.dtype].itemsize
-        per = elt * (self.S_q * self.D_qk + self.key_span() * (self.D_qk + self.D_v)
-                     + self.S_q * self.D_v) + 4 * self.S_q
-        return self.B * self.H * per
+        per_q = elt * (self.S_q * self.D_qk + self.S_q * self.D_v) + 4 * self.S_q
+        per_kv = elt * self.key_span() * (self.D_qk + self.D_v)
+        return self.B * (self.H * per_q + self.kv_heads * per_kv)
 
 
-def _x(name, B, H, S_q, S_k, D, causal, causal_offset, window, entry, seed, n_splits=0):
+def _x(name, B, H, S_q, S_k, D, causal, causal_offset, window, entry, seed, n_splits=0,
+       H_kv=0):
     return ExtWorkload(name, "bf16", B, H, S_q, S_k, D, D, causal, 1.0 / math.sqrt(D),
                        "normal", 1.0, 1.0, seed, causal_offset=causal_offset, window=window,
-                       entry=entry, n_splits=n_splits)
+                       entry=entry, n_splits=n_splits, H_kv=H_kv)
 
 
 # Workloads of the extended entry points (measured, not part of the target's
 # table): a chunk of 512 new queries against a 128k-key context and one
 # decoding query per sequence against 16k keys, both with the diagonal at
-# the bottom right, each with and without key chunks; and the long causal
-# case with a 4096-key sliding window.
+# the bottom right, each with and without key chunks; the decoding case
+# again with 8 K/V heads for the 32 query heads; and the long causal case
+# with a 4096-key sliding window.
 EXT_WORKLOADS = {
     w.name: w for w in [
         _x("bf16_b1h8_q512_k131072_d128_prefill_splitkv", 1, 8, 512, 131072, 128, True,
@@ -183,6 +200,8 @@ EXT_WORKLOADS = {
            16384 - 1, 0, "splitkv", 7),
         _x("bf16_b4h32_q1_k16384_d128_decode_nosplit", 4, 32, 1, 16384, 128, True,
            16384 - 1, 0, "ext", 7),
+        _x("bf16_b4h32kv8_q1_k16384_d128_decode_splitkv", 4, 32, 1, 16384, 128, True,
+           16384 - 1, 0, "splitkv", 9, H_kv=8),
         _x("bf16_b1h32_s16384_d128_causal_window4096", 1, 32, 16384, 16384, 128, True,
            0, 4096, "ext", 8),
     ]
