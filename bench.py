@@ -7,10 +7,17 @@ S_q=S_k=16384, D_qk=D_v=128 (the headline configuration).
 
 Prints ONE JSON line.  FLOPs per step follow the metric's count:
 2*B*H*S_q*S_k*(D_qk+D_v), halved for causal.  `roofline.achieved` divides
-that count by the kernel's average launch duration, timed with HIP events
-recorded on the stream the kernel runs on (torch's current stream, which is
-the stream the binding passes to the library).  `cpu_baseline` times the
-fp64 CPU oracle on a bounded row sample of the same workload.
+that count (or, for an HBM-bound launch, its algorithmic bytes) by the
+attention kernel's average launch duration: `steps` launches back to back
+after the timed steps, between two HIP events recorded on the stream the
+kernel runs on (torch's current stream, which is the stream the binding
+passes to the library).  `cpu_baseline` times the fp64 CPU oracle on a
+bounded row sample of the same workload.
+
+--workload also selects the extended entry points' workloads (key offset,
+sliding window, split-KV with its merge, grouped K/V heads); their FLOPs
+count 2*(D_qk+D_v) per visible (query, key) pair, and a split-KV step is
+the chunked attention launch followed by the merge launch.
 """
 from __future__ import annotations
 
@@ -323,11 +330,21 @@ def main():
         ev[i][-1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    sclk_mhz = measure_sclk(step, torch)
-
     launch_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps
                  for j in range(len(phases))]
-    kernel_ms = launch_ms[0]
+    # The attention launch alone, `steps` times back to back between two
+    # events: the per-launch events above also count each launch's dispatch
+    # gap, which is not small next to a launch of tens of microseconds.
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record(stream)
+    for _ in range(args.steps):
+        phases[0]()
+    a1.record(stream)
+    torch.cuda.synchronize()
+    kernel_ms = a0.elapsed_time(a1) / args.steps
+    extra["attn_ms_in_step"] = round(launch_ms[0], 4)
+    sclk_mhz = measure_sclk(step, torch)
+
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
