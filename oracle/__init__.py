@@ -57,6 +57,10 @@ def load_library(path: str) -> ctypes.CDLL:
                   ctypes.c_double, ctypes.c_int, i64, i64, i64, i64,
                   ctypes.POINTER(i64), i64, ctypes.c_int]
     g.restype = ctypes.c_int
+    h = lib.attn_ref_scaled_f64
+    h.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i64, i64, i64, i64, i64, i64, i64, i64,
+                  ctypes.c_int, ctypes.POINTER(i64), i64, ctypes.c_int]
+    h.restype = ctypes.c_int
     return lib
 
 
@@ -155,6 +159,43 @@ def attn_ref_ext(q, k, v, scale: float, causal: bool, causal_offset: int = 0,
                               rows_p, n_rows, int(nthreads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"attn_ref_ext_f64 failed with status {rc}")
+    return (o, lse, p) if want_probs else (o, lse)
+
+
+def attn_ref_scaled(q, k, v, q_scale, k_scale, q_block: int, k_block: int, causal: bool,
+                    rows=None, nthreads=None, want_probs: bool = False,
+                    lib: ctypes.CDLL | None = None):
+    """Base-2 attention with per-block scales: s_ij = q_scale[b,h,i//q_block]
+    * k_scale[b,h,j//k_block] * (q_i . k_j), weights 2^s_ij normalised per
+    row, LSE = ln sum_j 2^s_ij (natural log).  q_scale [B,H,ceil(S_q/q_block)],
+    k_scale [B,H,ceil(S_k/k_block)]; causal is top-left."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    qs = np.ascontiguousarray(q_scale, dtype=np.float64)
+    ks = np.ascontiguousarray(k_scale, dtype=np.float64)
+    B, H, S_q, D_qk = q.shape
+    S_k, D_v = k.shape[2], v.shape[3]
+    if k.shape != (B, H, S_k, D_qk) or v.shape[:3] != (B, H, S_k):
+        raise ValueError("inconsistent q/k/v shapes")
+    if qs.shape != (B, H, -(-S_q // q_block)) or ks.shape != (B, H, -(-S_k // k_block)):
+        raise ValueError("scale arrays do not match the block sizes")
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n_rows = rows.shape[0]
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    else:
+        n_rows, rows_p = S_q, None
+    o = np.empty((B, H, n_rows, D_v), dtype=np.float64)
+    lse = np.empty((B, H, n_rows), dtype=np.float64)
+    p = np.empty((B, H, n_rows, S_k), dtype=np.float64) if want_probs else None
+    lib = lib or _library()
+    rc = lib.attn_ref_scaled_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(p),
+                                 _ptr(qs), _ptr(ks), B, H, S_q, S_k, D_qk, D_v, int(q_block),
+                                 int(k_block), int(bool(causal)), rows_p, n_rows,
+                                 int(nthreads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"attn_ref_scaled_f64 failed with status {rc}")
     return (o, lse, p) if want_probs else (o, lse)
 
 

@@ -52,6 +52,16 @@
  *   address of attention_score on the same page (program p of batch p / H
  *   reads K head (p mod H) / (H / H_KV)); H_kv = H is the plain layout.
  *
+ * attn_ref_scaled_f64 is the base-2 attention with per-block Q and K scales
+ * of attention_forward_triton on the same page (`attentionRealBase2PerKeyScale`
+ * over `keyScale` built from Q_scale, one value per BLOCK_M query rows, and
+ * K_scale, one per BLOCK_N keys):
+ *     s_ij = Q_scale[b,h,i / q_block] * K_scale[b,h,j / k_block] * (Q_i . K_j)
+ *     O_i  = sum_j 2^(s_ij) V_j / sum_j 2^(s_ij),   LSE_i = ln sum_j 2^(s_ij).
+ *   2^x = exp(x ln 2), so this is the plain definition with the score
+ *   multiplied by ln 2 * Q_scale * K_scale (the definition's body is not
+ *   printed; this is the reading the name and the scale layout support).
+ *
  * Layout: contiguous row-major Q[B,H,S_q,D_qk], K[B,H,S_k,D_qk],
  * V[B,H,S_k,D_v], O[B,H,S_q,D_v], LSE[B,H,S_q] (all double).
  * With a row list, only those query rows are computed and O / LSE are
@@ -69,6 +79,8 @@ typedef struct {
     double scale;
     int causal;
     int64_t coff, window, kv_begin, kv_end;   /* key range of every row, see above */
+    const double *q_scale, *k_scale;          /* per-block scales, or NULL */
+    int64_t q_block, k_block;
     const int64_t *rows;
     int64_t n_rows;          /* rows computed per slice */
     int64_t first, last;     /* work items [first, last) over slices*n_rows */
@@ -114,6 +126,11 @@ static void oracle_row(const oracle_job *jb, int64_t slice, int64_t out_row,
         for (int64_t d = 0; d < jb->D_qk; ++d)
             dot += q[d] * k[j * jb->D_qk + d];
         s[j] = jb->scale * dot;
+        if (jb->q_scale)   /* the query block's and the key block's scales */
+            s[j] *= jb->q_scale[slice * ((jb->S_q + jb->q_block - 1) / jb->q_block) +
+                                i / jb->q_block] *
+                    jb->k_scale[slice * ((jb->S_k + jb->k_block - 1) / jb->k_block) +
+                                j / jb->k_block];
     }
     /* 2. score_max, seeded with -infinity */
     double m = -INFINITY;
@@ -166,6 +183,60 @@ static void *oracle_worker(void *arg)
     return NULL;
 }
 
+/* Validate the row list, then split the B*H*n_rows rows over threads. */
+static int run_jobs(const oracle_job *proto, int nthreads)
+{
+    int64_t n_rows = proto->n_rows;
+    if (proto->rows) {
+        if (n_rows < 1)
+            return 1;
+        for (int64_t r = 0; r < n_rows; ++r)
+            if (proto->rows[r] < 0 || proto->rows[r] >= proto->S_q)
+                return 1;
+    } else {
+        n_rows = proto->S_q;
+    }
+    int64_t total = proto->B * proto->H * n_rows;
+    if (nthreads < 1)
+        nthreads = 1;
+    if ((int64_t)nthreads > total)
+        nthreads = (int)total;
+
+    oracle_job *jobs = (oracle_job *)calloc((size_t)nthreads, sizeof(oracle_job));
+    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tids) {
+        free(jobs);
+        free(tids);
+        return 3;
+    }
+    int rc = 0, started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        oracle_job *jb = &jobs[t];
+        *jb = *proto;
+        jb->n_rows = n_rows;
+        jb->first = total * t / nthreads;
+        jb->last = total * (t + 1) / nthreads;
+        jb->status = 0;
+    }
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&tids[t], NULL, oracle_worker, &jobs[t]) != 0) {
+            rc = 2;
+            break;
+        }
+        started = t;
+    }
+    if (rc == 0)
+        oracle_worker(&jobs[0]);
+    for (int t = 1; t <= started; ++t)
+        pthread_join(tids[t], NULL);
+    for (int t = 0; t < nthreads && rc == 0; ++t)
+        if (jobs[t].status)
+            rc = jobs[t].status;
+    free(jobs);
+    free(tids);
+    return rc;
+}
+
 /*
  * attn_ref_ext_f64: the definition above with each row's keys restricted to
  * [max(kv_begin, i + causal_offset - window + 1) (window > 0 only),
@@ -194,60 +265,48 @@ int attn_ref_ext_f64(const double *Q, const double *K, const double *V,
         return 1;
     if (H_kv < 1 || H % H_kv != 0)
         return 1;
-    if (rows) {
-        if (n_rows < 1)
-            return 1;
-        for (int64_t r = 0; r < n_rows; ++r)
-            if (rows[r] < 0 || rows[r] >= S_q)
-                return 1;
-    } else {
-        n_rows = S_q;
-    }
-    int64_t total = B * H * n_rows;
-    if (nthreads < 1)
-        nthreads = 1;
-    if ((int64_t)nthreads > total)
-        nthreads = (int)total;
+    oracle_job proto = {0};
+    proto.Q = Q; proto.K = K; proto.V = V;
+    proto.O = O; proto.LSE = LSE; proto.P = P;
+    proto.B = B; proto.H = H; proto.H_kv = H_kv; proto.S_q = S_q; proto.S_k = S_k;
+    proto.D_qk = D_qk; proto.D_v = D_v;
+    proto.scale = scale; proto.causal = causal;
+    proto.coff = causal_offset; proto.window = window;
+    proto.kv_begin = kv_begin; proto.kv_end = kv_end;
+    proto.rows = rows; proto.n_rows = n_rows;
+    return run_jobs(&proto, nthreads);
+}
 
-    oracle_job *jobs = (oracle_job *)calloc((size_t)nthreads, sizeof(oracle_job));
-    pthread_t *tids = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
-    if (!jobs || !tids) {
-        free(jobs);
-        free(tids);
-        return 3;
-    }
-    int rc = 0, started = 0;
-    for (int t = 0; t < nthreads; ++t) {
-        oracle_job *jb = &jobs[t];
-        jb->Q = Q; jb->K = K; jb->V = V;
-        jb->O = O; jb->LSE = LSE; jb->P = P;
-        jb->B = B; jb->H = H; jb->H_kv = H_kv; jb->S_q = S_q; jb->S_k = S_k;
-        jb->D_qk = D_qk; jb->D_v = D_v;
-        jb->scale = scale; jb->causal = causal;
-        jb->coff = causal_offset; jb->window = window;
-        jb->kv_begin = kv_begin; jb->kv_end = kv_end;
-        jb->rows = rows; jb->n_rows = n_rows;
-        jb->first = total * t / nthreads;
-        jb->last = total * (t + 1) / nthreads;
-        jb->status = 0;
-    }
-    for (int t = 1; t < nthreads; ++t) {
-        if (pthread_create(&tids[t], NULL, oracle_worker, &jobs[t]) != 0) {
-            rc = 2;
-            break;
-        }
-        started = t;
-    }
-    if (rc == 0)
-        oracle_worker(&jobs[0]);
-    for (int t = 1; t <= started; ++t)
-        pthread_join(tids[t], NULL);
-    for (int t = 0; t < nthreads && rc == 0; ++t)
-        if (jobs[t].status)
-            rc = jobs[t].status;
-    free(jobs);
-    free(tids);
-    return rc;
+/*
+ * attn_ref_scaled_f64: base-2 attention with per-block scales (see the top
+ * of this file).  Q_scale is [B,H,ceil(S_q/q_block)], K_scale
+ * [B,H,ceil(S_k/k_block)]; causal is top-left as in attn_ref_f64.  Same
+ * return codes as attn_ref_ext_f64.
+ */
+int attn_ref_scaled_f64(const double *Q, const double *K, const double *V,
+                        double *O, double *LSE, double *P,
+                        const double *Q_scale, const double *K_scale,
+                        int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                        int64_t D_qk, int64_t D_v, int64_t q_block, int64_t k_block,
+                        int causal, const int64_t *rows, int64_t n_rows, int nthreads)
+{
+    if (!Q || !K || !V || !O || !Q_scale || !K_scale)
+        return 1;
+    if (B < 1 || H < 1 || S_q < 1 || S_k < 1 || D_qk < 1 || D_v < 1 || q_block < 1 ||
+        k_block < 1)
+        return 1;
+    oracle_job proto = {0};
+    proto.Q = Q; proto.K = K; proto.V = V;
+    proto.O = O; proto.LSE = LSE; proto.P = P;
+    proto.B = B; proto.H = H; proto.H_kv = H; proto.S_q = S_q; proto.S_k = S_k;
+    proto.D_qk = D_qk; proto.D_v = D_v;
+    proto.scale = log(2.0);   /* 2^x = e^(x ln 2) */
+    proto.causal = causal;
+    proto.coff = 0; proto.window = 0; proto.kv_begin = 0; proto.kv_end = S_k;
+    proto.q_scale = Q_scale; proto.k_scale = K_scale;
+    proto.q_block = q_block; proto.k_block = k_block;
+    proto.rows = rows; proto.n_rows = n_rows;
+    return run_jobs(&proto, nthreads);
 }
 
 /* The plain definition over every key (top-left causal when `causal`). */

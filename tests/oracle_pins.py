@@ -496,6 +496,74 @@ def pin_gqa_head_map(lib):
     _close(lse[:, 1::g], lse[:, 0::g], 0.0, "head map: equal heads LSE")
 
 
+def _scaled(lib, q, k, v, qs, ks, qb, kb, causal, **kw):
+    return oracle.attn_ref_scaled(q, k, v, qs, ks, qb, kb, causal, lib=lib, **kw)
+
+
+def pin_scaled_constant_scales(lib):
+    """Equal scales everywhere: base-2 attention with Q_scale = a and
+    K_scale = b is the plain definition with scale a * b * ln 2."""
+    rng = np.random.default_rng(61)
+    for B, H, S_q, S_k, D, qb, kb, causal in ((1, 2, 9, 13, 4, 3, 5, False),
+                                              (2, 1, 17, 11, 8, 4, 2, True),
+                                              (1, 1, 1, 1, 3, 1, 1, False)):
+        q, k, v = _randn(rng, B, H, S_q, D), _randn(rng, B, H, S_k, D), _randn(rng, B, H, S_k, 5)
+        a, b = 0.37, 1.9
+        qs = np.full((B, H, -(-S_q // qb)), a)
+        ks = np.full((B, H, -(-S_k // kb)), b)
+        o, lse = _scaled(lib, q, k, v, qs, ks, qb, kb, causal)
+        o_r, lse_r = _ref(lib, q, k, v, a * b * math.log(2.0), causal)
+        _close(o, o_r, 1e-12, f"constant scales {S_q}x{S_k} O")
+        _close(lse, lse_r, 1e-12, f"constant scales {S_q}x{S_k} LSE")
+
+
+def pin_scaled_brute_force(lib):
+    """40-digit sums of 2^s over every visible key, with per-block scales
+    drawn at random (negative and zero query scales, zero key scales)."""
+    rng = np.random.default_rng(62)
+    mpmath.mp.dps = 40
+    for trial in range(40):
+        S_q, S_k, D = int(rng.integers(1, 9)), int(rng.integers(1, 11)), int(rng.integers(1, 5))
+        qb, kb = int(rng.integers(1, 5)), int(rng.integers(1, 5))
+        causal = bool(rng.integers(0, 2))
+        q, k, v = _randn(rng, 1, 1, S_q, D), _randn(rng, 1, 1, S_k, D), _randn(rng, 1, 1, S_k, 2)
+        qs = rng.normal(size=(1, 1, -(-S_q // qb))) * 2
+        ks = np.abs(rng.normal(size=(1, 1, -(-S_k // kb)))) * 2
+        if trial % 5 == 0:
+            qs[..., 0] = 0.0
+            ks[..., -1] = 0.0
+        o, lse = _scaled(lib, q, k, v, qs, ks, qb, kb, causal)
+        for i in range(S_q):
+            n = min(i + 1, S_k) if causal else S_k
+            ws = []
+            for j in range(n):
+                dot = mpmath.fsum(mpmath.mpf(float(q[0, 0, i, d])) * mpmath.mpf(float(k[0, 0, j, d]))
+                              for d in range(D))
+                sc = mpmath.mpf(float(qs[0, 0, i // qb])) * mpmath.mpf(float(ks[0, 0, j // kb])) * dot
+                ws.append(mpmath.power(2, sc))
+            tot = mpmath.fsum(ws)
+            for e in range(2):
+                ref = mpmath.fsum(w * mpmath.mpf(float(v[0, 0, j, e])) for j, w in enumerate(ws)) / tot
+                assert abs(float(ref) - o[0, 0, i, e]) <= 1e-12, f"scaled brute force O {trial}"
+            assert abs(float(mpmath.log(tot)) - lse[0, 0, i]) <= 1e-12, f"scaled brute force LSE {trial}"
+
+
+def pin_scaled_zero_key_scales(lib):
+    """Every K scale 0: every score is 0, so O is the mean of the visible V
+    rows and LSE = ln(number of visible keys)."""
+    rng = np.random.default_rng(63)
+    S_q, S_k, D = 7, 10, 3
+    q, k, v = _randn(rng, 1, 2, S_q, D), _randn(rng, 1, 2, S_k, D), _randn(rng, 1, 2, S_k, 4)
+    qs = rng.normal(size=(1, 2, 4))
+    ks = np.zeros((1, 2, 4))
+    for causal in (False, True):
+        o, lse = _scaled(lib, q, k, v, qs, ks, 2, 3, causal)
+        for i in range(S_q):
+            n = min(i + 1, S_k) if causal else S_k
+            _close(o[:, :, i], v[:, :, :n].mean(axis=2), 1e-13, "zero key scales O")
+            _close(lse[:, :, i], np.full((1, 2), math.log(n)), 1e-13, "zero key scales LSE")
+
+
 PINS = [
     pin_library_sdpa,
     pin_highprec_unshifted,
@@ -518,4 +586,7 @@ PINS = [
     pin_ext_partition_merge,
     pin_gqa_library,
     pin_gqa_head_map,
+    pin_scaled_constant_scales,
+    pin_scaled_brute_force,
+    pin_scaled_zero_key_scales,
 ]

@@ -305,3 +305,30 @@ def test_gqa_partial():
         o_ref, lse_ref = ref_ext(q, k, v, 0.125, True, S_k - S_q, 0, s * ln,
                                  min(S_k, (s + 1) * ln))
         check(op[s], lp[s], o_ref, lse_ref, "bf16", f"gqa partial chunk {s}")
+
+
+@pytest.mark.parametrize("window", [1, 200, 1000])
+def test_window_and_complement_partition_causal(window):
+    """The sliding window (the `window` keys ending at the diagonal) and its
+    complement (the causal mask moved back by `window`) split every causal
+    row's keys in two: merging the two results gives plain causal attention,
+    and each part matches the oracle on its own."""
+    B, H, S, D = 1, 2, 1500, 128
+    q, k, v = random_inputs((B, H, S, D), (B, H, S, D), (B, H, S, D), "bf16", seed=71 + window)
+    qg, kg, vg = gpu(q, k, v)
+    ow, lw = tsd.attn_fwd_ext(qg, kg, vg, scale=0.09, causal=True, window=window)
+    oc, lc = tsd.attn_fwd_ext(qg, kg, vg, scale=0.09, causal=True, causal_offset=-window)
+    o_all, l_all = tsd.attn_fwd(qg, kg, vg, scale=0.09, causal=True)
+    torch.cuda.synchronize()
+    o_ref, l_ref = ref_ext(q, k, v, 0.09, True, 0, window)
+    check(to_np(ow), to_np(lw), o_ref, l_ref, "bf16", f"window {window}")
+    o_ref, l_ref = ref_ext(q, k, v, 0.09, True, -window)
+    check(to_np(oc), to_np(lc), o_ref, l_ref, "bf16", f"complement of window {window}")
+    # the merge of the two parts on the GPU is the plain causal result
+    parts_o = torch.stack([ow.float(), oc.float()])
+    parts_l = torch.stack([lw, lc])
+    om, lm = tsd.attn_merge(parts_o.contiguous(), parts_l.contiguous(), dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, l_ref = ref_ext(q, k, v, 0.09, True)
+    check(to_np(om), to_np(lm), o_ref, l_ref, "bf16", f"window {window} + complement merged")
+    check(to_np(o_all), to_np(l_all), o_ref, l_ref, "bf16", "plain causal")

@@ -51,6 +51,10 @@ MUTATIONS = [
     ("K/V head by modulo", "(slice % jb->H) / (jb->H / jb->H_kv)",
      "(slice % jb->H) % jb->H_kv"),
     ("K/V batch ignored", "(slice / jb->H) * jb->H_kv +", "0 * jb->H_kv +"),
+    ("query scale of the previous row's block", "i / jb->q_block]",
+     "(i > 0 ? i - 1 : 0) / jb->q_block]"),
+    ("key scale of the first block only", "j / jb->k_block]", "0]"),
+    ("natural base instead of 2", "proto.scale = log(2.0);", "proto.scale = 1.0;"),
 ]
 
 
