@@ -34,7 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # Published MI355X dense peaks (TFLOP/s) by compute dtype, and HBM bandwidth.
-PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3, "fp8_e4m3": 5033.2}
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "tiled_scaled_dot_amd", "csrc", "attn_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="oracle sample: every N-th query row of every head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sclk", action="store_true",
+                    help="skip the shader-clock reading (rocm-smi child process); for runs "
+                         "under a profiler whose preload initialises the GPU in every child")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps launches of a plain device "
                          "copy of this many MiB (counter calibration for HBM traffic)")
@@ -195,7 +198,7 @@ def measure_sclk(step, torch, limit_s: float = 15.0):
     return float(m.group(1)) if m else None
 
 
-def cpu_baseline(w, q, k, v, stride: int):
+def cpu_baseline(w, q, k, v, stride: int, scales=None):
     import numpy as np
 
     import oracle
@@ -205,9 +208,13 @@ def cpu_baseline(w, q, k, v, stride: int):
     kd = k.double().numpy()
     vd = v.double().numpy()
     threads = oracle.default_threads()
-    ext = hasattr(w, "entry")
+    ext = getattr(w, "entry", "fwd") in ("ext", "splitkv")
     t0 = time.perf_counter()
-    if ext:
+    if scales is not None:
+        oracle.attn_ref_scaled(qd, kd, vd, scales[0].double().numpy(),
+                               scales[1].double().numpy(), w.q_block, w.k_block, w.causal,
+                               rows=rows, nthreads=threads)
+    elif ext:
         oracle.attn_ref_ext(qd, kd, vd, w.scale, w.causal, causal_offset=w.causal_offset,
                             window=w.window, rows=rows, nthreads=threads)
     else:
@@ -259,19 +266,26 @@ def main():
 
     name = args.workload or HEADLINE
     w = ALL_WORKLOADS[name]
+    entry = getattr(w, "entry", "fwd")
     if args.n_splits is not None:
         if getattr(w, "entry", "fwd") != "splitkv":
             raise SystemExit("--n-splits applies to split-KV workloads only")
         w = w.with_(n_splits=args.n_splits)
     dev = torch.device("cuda:0")
-    q, k, v = make_inputs(w)
+    if entry == "scaled":
+        from tiled_scaled_dot_amd.workloads import scaled_inputs
+
+        q, k, v, q_sc, k_sc = scaled_inputs(w.B, w.H, w.S_q, w.S_k, w.D_qk, w.D_v, w.q_block,
+                                            w.k_block, w.qk_dtype, w.dtype, w.seed)
+        qsd, ksd = q_sc.to(dev), k_sc.to(dev)
+    else:
+        q, k, v = make_inputs(w)
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-    o = torch.empty(w.shape_o, dtype=qd.dtype, device=dev)
+    o = torch.empty(w.shape_o, dtype=vd.dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.S_q), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     flops = w.metric_flops()
     min_bytes = w.min_bytes()
-    entry = getattr(w, "entry", "fwd")
     extra = {}
 
     # A step is a list of launches; the first is the attention kernel (the
@@ -280,6 +294,10 @@ def main():
     if entry == "fwd":
         phases = [lambda: tsd.attn_fwd(qd, kd, vd, scale=w.scale, causal=w.causal, out=o,
                                        lse=lse, stream=stream)]
+        attn_bytes = min_bytes
+    elif entry == "scaled":
+        phases = [lambda: tsd.attn_fwd_scaled(qd, kd, vd, qsd, ksd, w.q_block, w.k_block,
+                                              causal=w.causal, out=o, lse=lse, stream=stream)]
         attn_bytes = min_bytes
     elif entry == "ext":
         phases = [lambda: tsd.attn_fwd_ext(qd, kd, vd, scale=w.scale, causal=w.causal,
@@ -343,11 +361,15 @@ def main():
     torch.cuda.synchronize()
     kernel_ms = a0.elapsed_time(a1) / args.steps
     extra["attn_ms_in_step"] = round(launch_ms[0], 4)
-    sclk_mhz = measure_sclk(step, torch)
+    sclk_mhz = None if args.no_sclk else measure_sclk(step, torch)
 
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    if entry == "scaled" and w.qk_dtype != w.dtype:
+        # Q K^T at the Q/K dtype's peak, P V at V's: the peak of the mix
+        f_qk, f_pv = w.D_qk / (w.D_qk + w.D_v), w.D_v / (w.D_qk + w.D_v)
+        peak = round(1.0 / (f_qk / PEAK_TFLOPS[w.qk_dtype] + f_pv / PEAK_TFLOPS[w.dtype]), 1)
     traffic = stored_traffic(name)
     # Roofline of the attention launch: MFMA when its FLOPs per algorithmic
     # byte exceed the ridge (peak / HBM bandwidth), else HBM.
@@ -362,13 +384,18 @@ def main():
         extra["merge_ms"] = round(launch_ms[1], 4)
         extra["merge_gbs"] = round(extra["merge_bytes_per_launch"] / (launch_ms[1] * 1e-3) / 1e9,
                                    1)
-    if entry != "fwd":
+    if entry == "scaled":
+        extra.update(entry=entry, qk_dtype=w.qk_dtype, q_block=w.q_block, k_block=w.k_block,
+                     mfma_peak_of_the_mix=peak)
+    elif entry != "fwd":
         extra.update(entry=entry, H_kv=w.kv_heads, causal_offset=w.causal_offset,
                      window=w.window, visible_pairs_per_slice=w.visible_pairs())
 
     result = {
         "metric": ("attention fwd TFLOP/s and % of MFMA peak (bf16 causal, S=16k, D=128)"
                    if entry == "fwd" else
+                   "attention fwd TFLOP/s, per-block scaled (metric FLOP count)"
+                   if entry == "scaled" else
                    "attention fwd TFLOP/s over visible (query, key) pairs"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
@@ -379,7 +406,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": (f"{w.qk_dtype}+{w.dtype}" if entry == "scaled" and w.qk_dtype != w.dtype
+                  else w.dtype),
         "data": "synthetic",
         "config": {
             "workload": name,
@@ -415,7 +443,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         del qd, kd, vd, o, lse
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_row_stride)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_row_stride,
+                                              (q_sc, k_sc) if entry == "scaled" else None)
     print(json.dumps(result), flush=True)
     return 0
 

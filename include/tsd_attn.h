@@ -49,7 +49,9 @@ enum {
 enum {
     TSD_F32 = 0,
     TSD_F16 = 1,
-    TSD_BF16 = 2
+    TSD_BF16 = 2,
+    TSD_FP8_E4M3 = 3     /* Q and K of attn_fwd_scaled only (OCP e4m3: 4 exponent
+                            bits, 3 mantissa bits, no infinities)            */
 };
 
 /* Launch plan, as chosen by the planner for one call (pure host data). */
@@ -243,6 +245,38 @@ int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float
                      int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
                      const tsd_mask *mask, int64_t n_splits,
                      void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_scaled — base-2 attention with per-block Q and K scales
+ * (VeriTile proof coverage, attention_forward_triton: the Q_scale value of
+ * the program's query block and the K_scale value of each key block multiply
+ * the scores, whose base-2 softmax weights V; `attentionRealBase2PerKeyScale`):
+ *
+ *   s_ij = Q_scale[b,h,i / q_block] * K_scale[b,h,j / k_block] * (Q_i . K_j)
+ *   O_i  = sum_j 2^(s_ij) V_j / sum_j 2^(s_ij)       (j <= i when causal)
+ *   LSE_i = ln sum_j 2^(s_ij)                        (natural log, as attn_fwd)
+ *
+ * The softmax scale and log2(e) belong in the block scales (a caller
+ * quantising to fp8 passes absmax/448 * scale * log2(e) as Q_scale).
+ *   Q [B,H,S_q,D_qk], K [B,H,S_k,D_qk] of `qk_dtype`: TSD_FP8_E4M3, or the
+ *       same 16-bit dtype as V.  fp8 scores run on the fp8 MFMA.
+ *   V [B,H,S_k,D_v], O [B,H,S_q,D_v] of `dtype` (TSD_F16 / TSD_BF16);
+ *       LSE [B,H,S_q] f32 or NULL.
+ *   Q_scale [B,H,ceil(S_q/q_block)] f32, any finite values;
+ *   K_scale [B,H,ceil(S_k/k_block)] f32, finite and >= 0 (a negative or NaN
+ *       key scale gives unspecified results: the kernel takes the row max of
+ *       the scaled scores as the scale times the raw row max).
+ *   q_block >= 1; k_block a multiple of 64 (the kernel's key tile).
+ * Fast path only: every buffer but the scales 16-byte aligned, D_v a
+ * multiple of 8, D_qk a multiple of 8 (16 for fp8); with fp8, D_qk in
+ * 65..128, or D_qk and D_v both at most 64 (else TSD_ERR_UNSUPPORTED).
+ * Statuses, ownership and threading as for attn_fwd.
+ */
+int attn_fwd_scaled(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                    const float *Q_scale, const float *K_scale,
+                    int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                    int64_t D_qk, int64_t D_v, int64_t q_block, int64_t k_block,
+                    int causal, int qk_dtype, int dtype, void *stream);
 
 /* attn_status_string — static text for a status code (never NULL). */
 const char *attn_status_string(int status);

@@ -13,7 +13,8 @@ import os
 
 __all__ = ["attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string",
            "attn_fwd_ext", "attn_fwd_partial", "attn_merge", "attn_splitkv_plan",
-           "attn_fwd_splitkv", "TsdMask", "TsdError", "library", "LIBRARY_PATH",
+           "attn_fwd_splitkv", "attn_fwd_scaled", "TsdMask", "TsdError", "library",
+           "LIBRARY_PATH",
            "DTYPE_CODES", "STATUS"]
 
 LIBRARY_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtsd_attn.so")
@@ -27,11 +28,11 @@ STATUS = {
     5: "TSD_ERR_ALIAS",
     6: "TSD_ERR_HIP",
 }
-DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8_e4m3": 3}
 
 EXPORTED = ("attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string",
             "attn_fwd_ext", "attn_fwd_partial", "attn_merge", "attn_splitkv_plan",
-            "attn_fwd_splitkv")
+            "attn_fwd_splitkv", "attn_fwd_scaled")
 
 
 class TsdError(RuntimeError):
@@ -122,6 +123,9 @@ def library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f,
                                      ci, ci, mp, i64, vp, i64, vp]
     lib.attn_fwd_splitkv.restype = ci
+    lib.attn_fwd_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                    i64, i64, ci, ci, ci, vp]
+    lib.attn_fwd_scaled.restype = ci
     _lib = lib
     return lib
 
@@ -344,6 +348,49 @@ def attn_fwd_splitkv(q, k, v, scale=None, causal=False, causal_offset=0, window=
                                 lse.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
                                 code, mask, n_splits, ws_ptr, ws_bytes,
                                 _stream(stream, q.device)))
+    return out, lse
+
+
+def attn_fwd_scaled_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, qs_ptr, ks_ptr, B, H, S_q, S_k,
+                        D_qk, D_v, q_block, k_block, causal, qk_dtype, dtype,
+                        stream=None) -> int:
+    return library().attn_fwd_scaled(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, qs_ptr, ks_ptr, B, H,
+                                     S_q, S_k, D_qk, D_v, q_block, k_block, int(bool(causal)),
+                                     _code(qk_dtype), _code(dtype), stream)
+
+
+def attn_fwd_scaled(q, k, v, q_scale, k_scale, q_block, k_block, causal=False, out=None,
+                    lse=None, stream=None):
+    """Base-2 attention with per-block scales: score = q_scale[b,h,i//q_block]
+    * k_scale[b,h,j//k_block] * (q_i . k_j), weights 2^score.  q, k:
+    float8_e4m3fn, or v's dtype (float16 / bfloat16); q_scale, k_scale:
+    float32 [B,H,ceil(S/block)], key scales >= 0; k_block a multiple of 64.
+    Returns O (v's dtype) and LSE (float32, natural log)."""
+    import torch
+
+    vcodes = {torch.float16: 1, torch.bfloat16: 2}
+    if v.dtype not in vcodes:
+        raise TypeError("v must be float16 or bfloat16")
+    qk_code = 3 if q.dtype == torch.float8_e4m3fn else vcodes.get(q.dtype)
+    if qk_code is None or k.dtype != q.dtype or (qk_code != 3 and q.dtype != v.dtype):
+        raise TypeError("q and k must be float8_e4m3fn, or v's dtype")
+    for name, t in (("q", q), ("k", k), ("v", v), ("q_scale", q_scale), ("k_scale", k_scale)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    B, H, S_q, D_qk = q.shape
+    S_k, D_v = k.shape[2], v.shape[3]
+    if tuple(k.shape) != (B, H, S_k, D_qk) or tuple(v.shape) != (B, H, S_k, D_v):
+        raise ValueError("inconsistent q/k/v shapes")
+    nq, nk = -(-S_q // q_block), -(-S_k // k_block)
+    if (tuple(q_scale.shape) != (B, H, nq) or tuple(k_scale.shape) != (B, H, nk)
+            or q_scale.dtype != torch.float32 or k_scale.dtype != torch.float32):
+        raise ValueError(f"q_scale must be float32 [{B},{H},{nq}] and k_scale [{B},{H},{nk}]")
+    out = _buffer(out, (B, H, S_q, D_v), v.dtype, v, "out")
+    lse = _buffer(lse, (B, H, S_q), torch.float32, v, "lse")
+    _check(attn_fwd_scaled_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), B, H, S_q,
+                               S_k, D_qk, D_v, q_block, k_block, causal, qk_code,
+                               vcodes[v.dtype], _stream(stream, v.device)))
     return out, lse
 
 

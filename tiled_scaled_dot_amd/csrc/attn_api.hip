@@ -125,6 +125,12 @@ tsd::KernelArgs base_args(const void *Q, const void *K, const void *V, void *O, 
     a.part_o_stride = 0;
     a.part_lse_stride = 0;
     a.q_per_head = (int32_t)S_q;
+    a.Q_scale = nullptr;
+    a.K_scale = nullptr;
+    a.q_block = 1;
+    a.q_scale_blocks = 0;
+    a.k_tiles_per_block = 1;
+    a.k_scale_blocks = 0;
     return a;
 }
 
@@ -492,6 +498,62 @@ extern "C" int attn_fwd_splitkv(const void *Q, const void *K, const void *V, voi
     st = launch_ext(Q, K, V, o_parts, l_parts, es, scale, causal, dtype, mk, n, len, true, s);
     if (st != TSD_OK) return st;
     return attn_merge(o_parts, l_parts, n, B, H, S_q, D_v, O, LSE, dtype, stream);
+}
+
+extern "C" int attn_fwd_scaled(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                               const float *Q_scale, const float *K_scale, int64_t B,
+                               int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
+                               int64_t q_block, int64_t k_block, int causal, int qk_dtype,
+                               int dtype, void *stream)
+{
+    if (!Q || !K || !V || !O || !Q_scale || !K_scale) return TSD_ERR_NULL;
+    if (B < 1 || H < 1 || S_q < 1 || S_k < 1 || D_qk < 1 || D_v < 1 || q_block < 1 ||
+        k_block < 1)
+        return TSD_ERR_SHAPE;
+    if (dtype != TSD_BF16 && dtype != TSD_F16) return TSD_ERR_UNSUPPORTED;
+    const bool qk8 = qk_dtype == TSD_FP8_E4M3;
+    if (!qk8 && qk_dtype != dtype) return TSD_ERR_UNSUPPORTED;
+    // V/O sizes and the grid as for attn_fwd; Q/K at their own element size
+    int st = check_shape(B, H, S_q, S_k, D_qk, D_v, dtype);
+    if (st != TSD_OK) return st;
+    const int64_t qkb = qk8 ? 1 : 2;
+    if (k_block % 64 != 0 || k_block > INT32_MAX || q_block > INT32_MAX)
+        return TSD_ERR_UNSUPPORTED;
+    if (D_v % 8 != 0 || D_qk % (16 / qkb) != 0) return TSD_ERR_UNSUPPORTED;
+    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, true);
+    if (qk8 && !(cfg.dqk_block == 128 || (cfg.dqk_block == 64 && cfg.dv_block == 64)))
+        return TSD_ERR_UNSUPPORTED;
+    for (uintptr_t p : {(uintptr_t)Q, (uintptr_t)K, (uintptr_t)V, (uintptr_t)O})
+        if (p % 16 != 0) return TSD_ERR_UNSUPPORTED;
+    if ((uintptr_t)LSE % 4 != 0 || (uintptr_t)Q_scale % 4 != 0 || (uintptr_t)K_scale % 4 != 0)
+        return TSD_ERR_UNSUPPORTED;
+
+    const uint64_t BH = (uint64_t)B * H;
+    const int64_t nqb = (S_q + q_block - 1) / q_block, nkb = (S_k + k_block - 1) / k_block;
+    const uint64_t q_bytes = BH * S_q * D_qk * qkb, k_bytes = BH * S_k * D_qk * qkb;
+    const uint64_t v_bytes = BH * S_k * D_v * 2, o_bytes = BH * S_q * D_v * 2;
+    const uint64_t l_bytes = LSE ? BH * S_q * 4 : 0;
+    const uint64_t qs_bytes = BH * nqb * 4, ks_bytes = BH * nkb * 4;
+    const void *ins[5] = {Q, K, V, Q_scale, K_scale};
+    const uint64_t in_bytes[5] = {q_bytes, k_bytes, v_bytes, qs_bytes, ks_bytes};
+    for (int i = 0; i < 5; ++i)
+        if (overlap(O, o_bytes, ins[i], in_bytes[i]) || overlap(LSE, l_bytes, ins[i], in_bytes[i]))
+            return TSD_ERR_ALIAS;
+    if (overlap(LSE, l_bytes, O, o_bytes)) return TSD_ERR_ALIAS;
+
+    tsd_plan plan;
+    fill_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype, true, &plan);
+    // the score scale lives in the block scales; Q enters unchanged
+    tsd::KernelArgs a = base_args(Q, K, V, O, LSE, S_q, S_k, D_qk, D_v, 1.0f, dtype, true, plan);
+    a.Q_scale = Q_scale;
+    a.K_scale = K_scale;
+    a.q_block = (int32_t)q_block;
+    a.q_scale_blocks = (int32_t)nqb;
+    a.k_tiles_per_block = (int32_t)(k_block / 64);
+    a.k_scale_blocks = (int32_t)nkb;
+    const hipError_t err = tsd::launch_attn_scaled(cfg, dtype, causal != 0, qk8, plan.grid, a,
+                                                   reinterpret_cast<hipStream_t>(stream));
+    return err == hipSuccess ? TSD_OK : TSD_ERR_HIP;
 }
 
 extern "C" const char *attn_status_string(int status)

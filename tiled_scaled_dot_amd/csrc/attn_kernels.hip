@@ -100,6 +100,21 @@ __device__ inline f32x16 mma16(u32x4 a, u32x4 b, f32x16 c)
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// fp8 (e4m3) scores: 32x32 outputs over 64 dims.  Each lane passes two
+// 16-byte chunks of its A row and of its B column; A and B share one lane
+// layout, so any assignment of dims to chunks that both operands follow
+// gives the full dot product.  The block scales of the instruction are left
+// at 1 (E8M0 127).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+__device__ inline f32x16 mma8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c)
+{
+    const i32x8 a = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                     (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+    const i32x8 b = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                     (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 __device__ inline f32x16 mma32(float a, float b, f32x16 c)
 {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -740,21 +755,22 @@ __device__ __attribute__((always_inline)) inline void sched_group()
 {
     if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
 }
-// NS score MFMAs (one K read each), then NP P V MFMAs (two transposed V
-// reads each).
-template <int NS, int NP>
+// NS score MFMAs (RS K reads and VS VALU slots each: an fp8 score MFMA
+// takes twice the cycles of a 16-bit one and reads two chunks), then NP
+// P V MFMAs (two transposed V reads each).
+template <int NS, int NP, int RS = 1, int VS = 1>
 __device__ __attribute__((always_inline)) inline void schedule_iteration()
 {
     if constexpr (TSD_SCHED) {
-        constexpr int LEAD = TSD_SCHED_LEAD < NS ? TSD_SCHED_LEAD : NS;
+        constexpr int LEAD = TSD_SCHED_LEAD < NS * RS ? TSD_SCHED_LEAD : NS * RS;
         constexpr int VA = TSD_SCHED_VALU;
         sched_group<0x100, LEAD>();
         sched_group<0x002, 2 * VA>();
         static_for<0, NS>([&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
             sched_group<0x008, 1>();
-            sched_group<0x100, (i + LEAD < NS) ? 1 : 2>();
-            sched_group<0x002, VA>();
+            sched_group<0x100, ((i + 1) * RS + LEAD <= NS * RS) ? RS : RS + 1>();
+            sched_group<0x002, VA * VS>();
         });
         static_for<0, NP>([&](auto ic) __attribute__((always_inline)) {
             sched_group<0x008, 1>();
@@ -764,13 +780,14 @@ __device__ __attribute__((always_inline)) inline void schedule_iteration()
     }
 }
 
-template <int DQ, int DV>
+template <int DQ, int DV, int QKB = 2>
 struct Fast16 {
     static constexpr FastShape SH = fast_shape(DQ, DV);
     static constexpr int NW = SH.waves, THREADS = 64 * SH.waves, BM = 32 * SH.waves;
     static constexpr int BN = 64;
-    static constexpr int KROW = DQ * 2, VROW = DV * 2; // bytes per row in LDS
-    static constexpr int KCH = DQ / 8, VCH = DV / 8;   // 16-byte chunks per row
+    static constexpr int KROW = DQ * QKB, VROW = DV * 2; // bytes per row in LDS (QKB bytes
+                                                         // per Q/K element: 2, or 1 for fp8)
+    static constexpr int KCH = KROW / 16, VCH = DV / 8;  // 16-byte chunks per row
     static constexpr int KT = BN * KROW, VT = BN * VROW;
     // Ring buffers of KS K tiles and VS V tiles.  Iteration t reads K(t+1)
     // (scores of the next tile) and V(t); after its barrier it refills the
@@ -795,12 +812,16 @@ struct Fast16 {
 // 64 banks to avoid conflicts.  16-byte chunk c of row r is stored at chunk
 // c ^ f(r):
 //   K (score A operand, 16 lanes read rows 0..15 of a block at one chunk):
-//     f(r) = r % 16 for 256-byte rows, (r / 2) % 8 for 128-byte rows;
+//     f(r) = r % 16 for 256-byte rows, (r / 2) % 8 for 128-byte rows,
+//     (r / 4) % 4 for 64-byte rows (fp8 keys of width 64);
 //   V (transposed reads, 32 lanes read 64 bytes from each of 4 consecutive
 //     rows): f(r) = 4 * (r % 4) for 256-byte rows, 4 * ((r / 2) % 2) for
 //     128-byte rows.
 template <int CHUNKS>
-__device__ inline int kswz(int row) { return CHUNKS == 16 ? (row & 15) : ((row >> 1) & 7); }
+__device__ inline int kswz(int row)
+{
+    return CHUNKS == 16 ? (row & 15) : CHUNKS == 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
 template <int CHUNKS>
 __device__ inline int vswz(int row) { return CHUNKS == 16 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2); }
 
@@ -865,16 +886,26 @@ __device__ inline void wait_loads()
 // window; rows that see no key get O = 0 and LSE = -inf.  OUT_F32: O is
 // written as f32 (partial results for a merge), chunk s at O + s *
 // part_o_stride and LSE + s * part_lse_stride.
-template <int DQ, int DV, bool CAUSAL, bool BF16, bool EXT = false, bool OUT_F32 = false>
+// SCALED: base-2 attention with per-block scales, score = Q_scale[query
+// block] * K_scale[key block] * (q . k) and weights 2^score; QK8: Q and K
+// are fp8 (e4m3) and the scores run on the fp8 MFMA (64 dims per
+// instruction, twice the 16-bit rate).
+template <int DQ, int DV, bool CAUSAL, bool BF16, bool EXT = false, bool OUT_F32 = false,
+          bool SCALED = false, bool QK8 = false>
 __global__ void __attribute__((amdgpu_flat_work_group_size(Fast16<DQ, DV>::THREADS,
                                                            Fast16<DQ, DV>::THREADS),
                                amdgpu_waves_per_eu(Fast16<DQ, DV>::SH.occ,
                                                    Fast16<DQ, DV>::SH.occ)))
 attn_fwd_fast16(KernelArgs p)
 {
-    using T = Fast16<DQ, DV>;
+    using T = Fast16<DQ, DV, QK8 ? 1 : 2>;
     constexpr int BN = T::BN;
+    constexpr int QKB = QK8 ? 1 : 2;          // bytes per Q/K element
+    constexpr int KREADS = T::KCH / 2;        // 16-byte K reads per lane per 32-key block
     static_assert(EXT || !OUT_F32, "f32 output only in the extended kernel");
+    static_assert(!(SCALED && EXT), "per-block scales use the plain visibility");
+    static_assert(SCALED || !QK8, "fp8 keys come with their block scales");
+    static_assert(!QK8 || DQ % 64 == 0, "fp8 scores take 64 dims per MFMA");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -911,8 +942,8 @@ attn_fwd_fast16(KernelArgs p)
         ntiles = kv_tiles_for(qb, T::BM, BN, p.S_q, p.S_k, CAUSAL);
     }
 
-    const uint32_t q_bytes = (uint32_t)p.S_q * p.D_qk * 2;
-    const uint32_t k_bytes = (uint32_t)p.S_k * p.D_qk * 2;
+    const uint32_t q_bytes = (uint32_t)p.S_q * p.D_qk * QKB;
+    const uint32_t k_bytes = (uint32_t)p.S_k * p.D_qk * QKB;
     const uint32_t v_bytes = (uint32_t)p.S_k * p.D_v * 2;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(static_cast<const uint8_t *>(p.Q) + (size_t)slice * q_bytes, q_bytes);
@@ -925,7 +956,8 @@ attn_fwd_fast16(KernelArgs p)
     for (int j = 0; j < T::K_PER_W; ++j) {
         const int P = (wave * T::K_PER_W + j) * 64 + lane;   // chunk slot in the K tile
         const int row = P / T::KCH, c = (P % T::KCH) ^ kswz<T::KCH>(row);
-        koff[j] = c * 8 < p.D_qk ? (uint32_t)(row * p.D_qk + c * 8) * 2 : kOutOfRange;
+        constexpr int EPC = 16 / QKB;   // elements per 16-byte chunk
+        koff[j] = c * EPC < p.D_qk ? (uint32_t)(row * p.D_qk + c * EPC) * QKB : kOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < T::V_PER_W; ++j) {
@@ -944,7 +976,7 @@ attn_fwd_fast16(KernelArgs p)
     // check still drops rows past the slice.
     auto issue_k = [&](int t, auto slot_c) __attribute__((always_inline)) {
         constexpr uint32_t sl = decltype(slot_c)::value * T::KT;
-        const u32x4 r = tile_rsrc(rk, (uint32_t)(t_first + t) * BN * p.D_qk * 2);
+        const u32x4 r = tile_rsrc(rk, (uint32_t)(t_first + t) * BN * p.D_qk * QKB);
 #pragma unroll
         for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + sl + j * 1024, koff[j], r);
     };
@@ -1000,27 +1032,43 @@ attn_fwd_fast16(KernelArgs p)
             if (j - 1 < ntiles) issue_v(j - 1, IC<j - 1>{});
     });
 
-    // ---- Q fragment (B operand of S^T = K Q^T): query qi, dims 16st + 8hh + 0..7
-    u32x4 qf[DQ / 16];
+    // ---- per-row scale (SCALED): this lane's query block's Q scale, folded
+    // into the exponent factor; a negative scale flips Q's sign, a zero one
+    // zeroes Q (as the global scale does in the plain kernel).
+    float c = p.c;
+    uint32_t q_xor = p.q_xor, q_and = p.q_and;
+    if constexpr (SCALED) {
+        float qs = 1.0f;
+        if (qi < p.S_q) qs = p.Q_scale[(size_t)slice * p.q_scale_blocks + qi / p.q_block];
+        c = qs == 0.0f ? 1.0f : __builtin_fabsf(qs);
+        q_xor = qs < 0.0f ? (QK8 ? 0x80808080u : 0x80008000u) : 0u;
+        q_and = qs == 0.0f ? 0u : 0xffffffffu;
+    }
+
+    // ---- Q fragment (B operand of S^T = K Q^T): query qi, 16-byte chunk
+    // 2j + hh of the row in register group j (16-bit: dims 16j + 8hh + 0..7,
+    // one MFMA each; fp8: dims 32j + 16hh + 0..15, two groups per MFMA).
+    constexpr int QCH = DQ * QKB / 32;   // 16-byte chunks per lane
+    u32x4 qf[QCH];
 #pragma unroll
-    for (int st = 0; st < DQ / 16; ++st) {
-        const int d0 = st * 16 + hh * 8;
-        const uint32_t off = d0 < p.D_qk ? (uint32_t)(qi * p.D_qk + d0) * 2 : kOutOfRange;
+    for (int j = 0; j < QCH; ++j) {
+        const int d0 = (2 * j + hh) * (16 / QKB);
+        const uint32_t off = d0 < p.D_qk ? (uint32_t)(qi * p.D_qk + d0) * QKB : kOutOfRange;
         u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-        x = (x ^ p.q_xor) & p.q_and;
+        x = (x ^ q_xor) & q_and;
         if (d0 >= p.D_qk) x = u32x4{0u, 0u, 0u, 0u};
-        qf[st] = x;
+        qf[j] = x;
     }
 
     // ---- per-lane LDS read addresses in stage 0, computed once
     // K (score A operand): row 32kb + sigma(l32), logical chunk 2st + hh.
     // The swizzle depends on the row only through bits the kb term does not
     // touch, so the kb offset is an immediate.
-    uint32_t kro[DQ / 16];
+    uint32_t kro[KREADS];
     {
         const int krow = sigma(l32);
 #pragma unroll
-        for (int st = 0; st < DQ / 16; ++st)
+        for (int st = 0; st < KREADS; ++st)
             kro[st] = lds_address(smem) +
                       (uint32_t)(krow * T::KROW + ((2 * st + hh) ^ kswz<T::KCH>(krow)) * 16);
     }
@@ -1042,22 +1090,35 @@ attn_fwd_fast16(KernelArgs p)
     f32x16 o[DV / 32];
 #pragma unroll
     for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
-    const float c = p.c;
-    float m = neg_inf();   // running max of the raw scores of this query
+    float m = neg_inf();   // running max of the raw scores of this query (SCALED:
+                           // of the scores times their key block's scale)
     float l = 0.0f;        // running sum of this lane's half of the keys
 
     // S^T of the key tile staged at `so` (two 32-key blocks).
     auto scores = [&](uint32_t so, f32x16 (&out)[2]) __attribute__((always_inline)) {
         out[0] = f32x16{};
         out[1] = f32x16{};
+        typedef const __attribute__((address_space(3))) u32x4 lds_u32x4;
+        if constexpr (QK8) {
 #pragma unroll
-        for (int st = 0; st < DQ / 16; ++st) {
-            const auto *k0 = reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
-                lds_ptr(kro[st] + so));
-            const auto *k1 = reinterpret_cast<const __attribute__((address_space(3))) u32x4 *>(
-                lds_ptr(kro[st] + so) + 32 * T::KROW);
-            out[0] = mma16<BF16>(*k0, qf[st], out[0]);
-            out[1] = mma16<BF16>(*k1, qf[st], out[1]);
+            for (int st = 0; st < DQ / 64; ++st) {
+                const u32x4 a0 = *reinterpret_cast<lds_u32x4 *>(lds_ptr(kro[2 * st] + so));
+                const u32x4 a1 = *reinterpret_cast<lds_u32x4 *>(lds_ptr(kro[2 * st + 1] + so));
+                const u32x4 b0 = *reinterpret_cast<lds_u32x4 *>(
+                    lds_ptr(kro[2 * st] + so) + 32 * T::KROW);
+                const u32x4 b1 = *reinterpret_cast<lds_u32x4 *>(
+                    lds_ptr(kro[2 * st + 1] + so) + 32 * T::KROW);
+                out[0] = mma8(a0, a1, qf[2 * st], qf[2 * st + 1], out[0]);
+                out[1] = mma8(b0, b1, qf[2 * st], qf[2 * st + 1], out[1]);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < DQ / 16; ++st) {
+                const auto *k0 = reinterpret_cast<lds_u32x4 *>(lds_ptr(kro[st] + so));
+                const auto *k1 = reinterpret_cast<lds_u32x4 *>(lds_ptr(kro[st] + so) + 32 * T::KROW);
+                out[0] = mma16<BF16>(*k0, qf[st], out[0]);
+                out[1] = mma16<BF16>(*k1, qf[st], out[1]);
+            }
         }
     };
     auto lane_max = [](const f32x16 (&x)[2]) __attribute__((always_inline)) {
@@ -1088,14 +1149,14 @@ attn_fwd_fast16(KernelArgs p)
     };
     // P = 2^(s c - m c) for one 32-key block, packed to 16 bits; the row sum
     // is taken over the f32 values so that LSE keeps f32 accuracy.
-    auto probs = [&](const f32x16 &sb, float mc, u32x4 (&pb)[2], float &rs) __attribute__((always_inline)) {
+    auto probs = [&](const f32x16 &sb, float ct, float mc, u32x4 (&pb)[2], float &rs) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             uint32_t w[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float p0 = fast_exp2(__builtin_fmaf(sb[8 * u + 2 * j], c, -mc));
-                const float p1 = fast_exp2(__builtin_fmaf(sb[8 * u + 2 * j + 1], c, -mc));
+                const float p0 = fast_exp2(__builtin_fmaf(sb[8 * u + 2 * j], ct, -mc));
+                const float p1 = fast_exp2(__builtin_fmaf(sb[8 * u + 2 * j + 1], ct, -mc));
                 rs += p0 + p1;
                 w[j] = pack2<BF16>(p0, p1);
             }
@@ -1129,8 +1190,20 @@ attn_fwd_fast16(KernelArgs p)
     f32x16 sc[2][2];     // scores of tiles t and t+1, alternating by parity
     float mxs[2];        // their row maxima (both lane halves)
     bool grows[2];       // some row's max exceeds m by more than 2^kTau (unmasked tiles)
+    // SCALED: the key block scale of tile t (wave-uniform, a scalar load).
+    // Scales are >= 0, so the max of the scaled scores is the scale times
+    // the max of the raw ones; a zero scale is raised to the smallest normal
+    // float, which keeps masked scores at -inf and changes no result.
+    float kss[2] = {1.0f, 1.0f};
+    auto key_scale = [&](int t) __attribute__((always_inline)) {
+        const int tt = min(t, ntiles - 1);
+        const float v = p.K_scale[(size_t)slice * p.k_scale_blocks + tt / p.k_tiles_per_block];
+        return fmaxf(v, 1.17549435e-38f);
+    };
+    if constexpr (SCALED) kss[0] = key_scale(0);
     scores(0, sc[0]);
     mxs[0] = max_halves(lane_max(sc[0]));
+    if constexpr (SCALED) mxs[0] *= kss[0];
     grows[0] = true;     // m is still -inf
 
     // ---- one iteration of the main loop, software pipelined: iteration t
@@ -1152,6 +1225,7 @@ attn_fwd_fast16(KernelArgs p)
 
         float mx = mxs[u & 1];
         bool grow_any = grows[u & 1];
+        if constexpr (SCALED) kss[(u + 1) & 1] = key_scale(t + 1);
         if (active) {
             // masks: keys >= S_k; keys after the query when causal (in the
             // extended kernel: keys outside the row's [lo_i, hi_i))
@@ -1182,6 +1256,7 @@ attn_fwd_fast16(KernelArgs p)
                         s[kb][r] = keep ? s[kb][r] : neg_inf();
                     }
                 mx = max_halves(lane_max(s));
+                if constexpr (SCALED) mx *= kss[u & 1];
                 grow_any = __builtin_amdgcn_ballot_w64((mx - m) * c > kTau) != 0;
             }
             // running max; rescale only when a row's max grows by > 2^kTau
@@ -1226,20 +1301,26 @@ attn_fwd_fast16(KernelArgs p)
             if (m == neg_inf()) mc = 0.0f;   // row without keys so far: every P is 0
         float rs = 0.0f;
         u32x4 pb0[2], pb1[2];
+        float ct = c;   // exponent factor of this tile's raw scores
+        if constexpr (SCALED) ct = c * kss[u & 1];
         // phase A: scores of tile t+1 (garbage past the last tile, unused) || P of block 0
         scores(so1, sn);
-        probs(s[0], mc, pb0, rs);
+        probs(s[0], ct, mc, pb0, rs);
         // phase B1: O += V P for block 0 || P of block 1
         pv_block(so, 0, pb0);
-        probs(s[1], mc, pb1, rs);
+        probs(s[1], ct, mc, pb1, rs);
         // phase B2: O += V P for block 1 || lane max of the next scores
         pv_block(so, 1, pb1);
         // the next tile's row max and its rescale decision, decided here
         // beside the P V MFMAs (m no longer changes in this iteration)
         mxs[(u + 1) & 1] = max_halves(lane_max(sn));
+        if constexpr (SCALED) mxs[(u + 1) & 1] *= kss[(u + 1) & 1];
         grows[(u + 1) & 1] = __builtin_amdgcn_ballot_w64((mxs[(u + 1) & 1] - m) * c > kTau) != 0;
         l += rs;
-        schedule_iteration<2 * (DQ / 16), 4 * (DV / 32)>();
+        if constexpr (QK8)
+            schedule_iteration<2 * (DQ / 64), 4 * (DV / 32), 2, 2>();
+        else
+            schedule_iteration<2 * (DQ / 16), 4 * (DV / 32)>();
     };
 
     for (int t0 = 0; t0 < ntiles; t0 += T::U) {
@@ -1331,6 +1412,38 @@ hipError_t dispatch_fast_ext(int dtype, bool causal, bool out_f32, int64_t grid,
     return causal
                ? launch(attn_fwd_fast16<DQ, DV, true, false, true, false>, grid, a, s, threads)
                : launch(attn_fwd_fast16<DQ, DV, false, false, true, false>, grid, a, s, threads);
+}
+
+template <int DQ, int DV>
+hipError_t dispatch_fast_scaled(int dtype, bool causal, bool qk8, int64_t grid,
+                                const KernelArgs &a, hipStream_t s)
+{
+    constexpr int threads = Fast16<DQ, DV>::THREADS;
+    // fp8 keys: a K tile of 64 x DQ bytes must give each wave at least one
+    // 1 KB load (DQ = 128, or DQ = 64 with the 4-wave shape)
+    if constexpr (DQ == 128 || (DQ == 64 && DV == 64)) {
+        if (qk8) {
+            if (dtype == TSD_BF16)
+                return causal ? launch(attn_fwd_fast16<DQ, DV, true, true, false, false, true, true>,
+                                       grid, a, s, threads)
+                              : launch(attn_fwd_fast16<DQ, DV, false, true, false, false, true, true>,
+                                       grid, a, s, threads);
+            return causal ? launch(attn_fwd_fast16<DQ, DV, true, false, false, false, true, true>,
+                                   grid, a, s, threads)
+                          : launch(attn_fwd_fast16<DQ, DV, false, false, false, false, true, true>,
+                                   grid, a, s, threads);
+        }
+    }
+    if (qk8) return hipErrorInvalidValue;
+    if (dtype == TSD_BF16)
+        return causal ? launch(attn_fwd_fast16<DQ, DV, true, true, false, false, true, false>, grid,
+                               a, s, threads)
+                      : launch(attn_fwd_fast16<DQ, DV, false, true, false, false, true, false>,
+                               grid, a, s, threads);
+    return causal ? launch(attn_fwd_fast16<DQ, DV, true, false, false, false, true, false>, grid, a,
+                           s, threads)
+                  : launch(attn_fwd_fast16<DQ, DV, false, false, false, false, true, false>, grid,
+                           a, s, threads);
 }
 
 // ====================================================================
@@ -1482,6 +1595,18 @@ hipError_t launch_attn_ext(const TileConfig &cfg, int dtype, bool causal, bool o
     case 1: return dispatch_fast_ext<64, 128>(dtype, causal, out_f32, grid, args, stream);
     case 2: return dispatch_fast_ext<128, 64>(dtype, causal, out_f32, grid, args, stream);
     default: return dispatch_fast_ext<128, 128>(dtype, causal, out_f32, grid, args, stream);
+    }
+}
+
+hipError_t launch_attn_scaled(const TileConfig &cfg, int dtype, bool causal, bool qk8,
+                              int64_t grid, const KernelArgs &args, hipStream_t stream)
+{
+    if (!cfg.fast) return hipErrorInvalidValue;
+    switch ((cfg.dqk_block == 128 ? 2 : 0) + (cfg.dv_block == 128 ? 1 : 0)) {
+    case 0: return dispatch_fast_scaled<64, 64>(dtype, causal, qk8, grid, args, stream);
+    case 1: return dispatch_fast_scaled<64, 128>(dtype, causal, false, grid, args, stream);
+    case 2: return dispatch_fast_scaled<128, 64>(dtype, causal, qk8, grid, args, stream);
+    default: return dispatch_fast_scaled<128, 128>(dtype, causal, qk8, grid, args, stream);
     }
 }
 

@@ -38,6 +38,12 @@ struct KernelArgs {
     int32_t q_per_head;         // row r of a slice is query position r % q_per_head (grouped
                                 // heads: a slice holds the rows of every query head that
                                 // shares its K/V head); S_q when each slice is one head
+    // Per-block scales of the scaled kernels (null otherwise): Q_scale
+    // [slices][q_scale_blocks], one per q_block rows; K_scale
+    // [slices][k_scale_blocks], one per k_tiles_per_block 64-key tiles.
+    const float *Q_scale;
+    const float *K_scale;
+    int32_t q_block, q_scale_blocks, k_tiles_per_block, k_scale_blocks;
 };
 
 // Keys a workgroup of query positions [q0, q_end) sees inside the key range
@@ -139,6 +145,12 @@ struct MergeArgs {
     int32_t D_v, n_parts;
     int32_t groups;           // ceil(D_v / 4) threads per row
 };
+
+// The per-block scaled form of the LDS-direct kernel (base-2 weights; Q and
+// K in `dtype` or, with qk8, fp8 e4m3).  qk8 needs a Q/K block of 128, or 64
+// with a V block of 64.
+hipError_t launch_attn_scaled(const TileConfig &cfg, int dtype, bool causal, bool qk8,
+                              int64_t grid, const KernelArgs &args, hipStream_t stream);
 
 // vec: D_v % 4 == 0 and the buffers allow 16-byte (f32) / 8-byte (16-bit) access.
 hipError_t launch_merge(int dtype, bool vec, const MergeArgs &args, hipStream_t stream);

@@ -207,7 +207,44 @@ EXT_WORKLOADS = {
     ]
 }
 
-ALL_WORKLOADS = {**WORKLOADS, **EXT_WORKLOADS}
+@dataclass(frozen=True)
+class ScaledWorkload(Workload):
+    """A workload of attn_fwd_scaled: base-2 weights with per-block scales
+    (Q_scale per q_block query rows, K_scale per k_block keys); Q and K in
+    ``qk_dtype`` (fp8_e4m3 or the 16-bit dtype), V and O in ``dtype``.
+    Inputs come from ``scaled_inputs`` (the fp8 case quantises N(0,1) draws
+    per block)."""
+    q_block: int = 128
+    k_block: int = 64
+    qk_dtype: str = "fp8_e4m3"
+    entry: str = "scaled"
+
+    def min_bytes(self) -> int:
+        qkb = 1 if self.qk_dtype == "fp8_e4m3" else DTYPES[self.qk_dtype].itemsize
+        elt = DTYPES[self.dtype].itemsize
+        nq, nk = -(-self.S_q // self.q_block), -(-self.S_k // self.k_block)
+        per = (qkb * (self.S_q + self.S_k) * self.D_qk + elt * (self.S_k + self.S_q) * self.D_v
+               + 4 * self.S_q + 4 * (nq + nk))
+        return self.B * self.H * per
+
+
+def _s(name, qk_dtype, causal, seed):
+    return ScaledWorkload(name, "bf16", 1, 32, 16384, 16384, 128, 128, causal,
+                          1.0 / math.sqrt(128), "normal", 1.0, 1.0, seed, q_block=128,
+                          k_block=64, qk_dtype=qk_dtype)
+
+
+# The long causal and non-causal cases with per-block scales: fp8 Q/K (the
+# scores on the fp8 MFMA) and bf16 Q/K (the same chain at the 16-bit rate).
+SCALED_WORKLOADS = {
+    w.name: w for w in [
+        _s("fp8qk_b1h32_s16384_d128_causal_scaled", "fp8_e4m3", True, 10),
+        _s("fp8qk_b1h32_s16384_d128_scaled", "fp8_e4m3", False, 10),
+        _s("bf16_b1h32_s16384_d128_causal_scaled", "bf16", True, 10),
+    ]
+}
+
+ALL_WORKLOADS = {**WORKLOADS, **EXT_WORKLOADS, **SCALED_WORKLOADS}
 
 
 def make_inputs(w: Workload, device="cpu"):
@@ -239,6 +276,51 @@ def random_inputs(shape_q, shape_k, shape_v, dtype: str, seed: int,
     k = (torch.randn(shape_k, generator=g) * sigma).to(dt)
     v = torch.randn(shape_v, generator=g).to(dt)
     return q, k, v
+
+
+def scaled_inputs(B, H, S_q, S_k, D_qk, D_v, q_block, k_block, qk_dtype: str, v_dtype: str,
+                  seed: int, sigma: float = 1.0, sm_scale=None, scale_jitter: bool = False):
+    """Inputs of the per-block scaled attention (seeded).
+
+    Draws Q, K, V like ``random_inputs`` (normal, Q and K with std
+    ``sigma``).  For ``qk_dtype == "fp8_e4m3"`` each block of q_block query
+    rows (k_block keys) is divided by its absolute maximum / 448 and rounded
+    to float8_e4m3fn; that factor times ``sm_scale * log2(e)`` (default
+    sm_scale 1/sqrt(D_qk)) is the block's Q scale, the factor alone its K
+    scale: the caller's quantisation step, which the method takes as given.
+    For a 16-bit ``qk_dtype`` Q and K are rounded to it and the scales are
+    ``sm_scale * log2(e)`` and 1, each times a factor drawn from [0.5, 1.5)
+    per block when ``scale_jitter``.  Returns (q, k, v, q_scale, k_scale) on
+    the CPU; the scales are float32 [B,H,blocks]."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((B, H, S_q, D_qk), generator=g) * sigma
+    k = torch.randn((B, H, S_k, D_qk), generator=g) * sigma
+    v = torch.randn((B, H, S_k, D_v), generator=g)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D_qk)
+    c = sm_scale * 1.4426950408889634
+    nq, nk = -(-S_q // q_block), -(-S_k // k_block)
+
+    def per_block(x, blk, n):
+        pad = n * blk - x.shape[2]
+        xp = torch.nn.functional.pad(x, (0, 0, 0, pad))
+        amax = xp.abs().reshape(B, H, n, blk * x.shape[3]).amax(-1)
+        return torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+
+    if qk_dtype == "fp8_e4m3":
+        fq, fk = per_block(q, q_block, nq), per_block(k, k_block, nk)
+        q8 = (q / fq.repeat_interleave(q_block, dim=2)[:, :, :S_q, None]).to(torch.float8_e4m3fn)
+        k8 = (k / fk.repeat_interleave(k_block, dim=2)[:, :, :S_k, None]).to(torch.float8_e4m3fn)
+        q_scale, k_scale = (fq * c).float(), fk.float()
+        q, k = q8, k8
+    else:
+        q, k = q.to(DTYPES[qk_dtype]), k.to(DTYPES[qk_dtype])
+        q_scale = torch.full((B, H, nq), c)
+        k_scale = torch.ones((B, H, nk))
+        if scale_jitter:
+            q_scale = q_scale * (0.5 + torch.rand((B, H, nq), generator=g))
+            k_scale = k_scale * (0.5 + torch.rand((B, H, nk), generator=g))
+    return q, k, v.to(DTYPES[v_dtype]), q_scale.float().contiguous(), k_scale.float().contiguous()
 
 
 def sample_rows(S_q: int, block_m: int = 128, stride: int = 16):
