@@ -23,6 +23,14 @@
 
 #include <stdint.h>
 
+/* The library is built with hidden visibility; only these entry points are
+ * exported. */
+#if defined(__GNUC__) || defined(__clang__)
+#define TSD_API __attribute__((visibility("default")))
+#else
+#define TSD_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -93,7 +101,7 @@ typedef struct tsd_plan {
  * threads.  Only rows i < S_q and columns e < D_v of O, and only the B*H*S_q
  * entries of LSE, are written.  Returns a TSD_* status.
  */
-int attn_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
+TSD_API int attn_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
              int64_t B, int64_t H, int64_t S_q, int64_t S_k,
              int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
              void *stream);
@@ -104,7 +112,7 @@ int attn_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
  * here, so `vector_io` reports what aligned buffers would get.  Returns the
  * same shape/dtype statuses as attn_fwd (TSD_ERR_NULL if out is NULL).
  */
-int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+TSD_API int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
                   int64_t D_qk, int64_t D_v, int causal, int dtype,
                   tsd_plan *out);
 
@@ -114,7 +122,7 @@ int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
  * tiles it visits, exactly as the kernel derives them (host only).
  * Returns TSD_ERR_SHAPE if `block` is out of range.
  */
-int attn_fwd_plan_block(const tsd_plan *plan, int64_t S_q, int64_t S_k,
+TSD_API int attn_fwd_plan_block(const tsd_plan *plan, int64_t S_q, int64_t S_k,
                         int64_t block, int64_t *q_block, int64_t *slice,
                         int64_t *kv_steps);
 
@@ -172,7 +180,7 @@ typedef struct tsd_mask {
  * of `dtype`, LSE [B,H,S_q] f32 (may be NULL).  Same statuses as attn_fwd,
  * plus the mask and fast-path conditions above.
  */
-int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
+TSD_API int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
                  int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                  int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
                  const tsd_mask *mask, void *stream);
@@ -191,7 +199,7 @@ int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LS
  * Merging the n_splits results with attn_merge gives attn_fwd_ext's result
  * up to rounding.
  */
-int attn_fwd_partial(const void *Q, const void *K, const void *V,
+TSD_API int attn_fwd_partial(const void *Q, const void *K, const void *V,
                      float *O_parts, float *LSE_parts,
                      int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                      int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
@@ -211,7 +219,7 @@ int attn_fwd_partial(const void *Q, const void *K, const void *V,
  * LSE [B,H,S_q] f32 or NULL.  Any D_v in 1..128.  Outputs must not overlap
  * the parts (TSD_ERR_ALIAS).
  */
-int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
+TSD_API int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
                int64_t B, int64_t H, int64_t S_q, int64_t D_v,
                void *O, float *LSE, int dtype, void *stream);
 
@@ -224,7 +232,7 @@ int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
  * length in keys and the workspace bytes attn_fwd_splitkv needs (0 when a
  * single chunk is used: then no workspace is touched).
  */
-int attn_splitkv_plan(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
+TSD_API int attn_splitkv_plan(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                       int64_t D_qk, int64_t D_v, int causal, int dtype,
                       const tsd_mask *mask, int64_t n_splits,
                       int64_t *splits_out, int64_t *split_len_out,
@@ -240,7 +248,7 @@ int attn_splitkv_plan(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S
  * results between the two launches; it may be NULL when the plan needs
  * none.  Too small a workspace: TSD_ERR_SHAPE.
  */
-int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
+TSD_API int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
                      int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
                      int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
                      const tsd_mask *mask, int64_t n_splits,
@@ -272,14 +280,14 @@ int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float
  * 65..128, or D_qk and D_v both at most 64 (else TSD_ERR_UNSUPPORTED).
  * Statuses, ownership and threading as for attn_fwd.
  */
-int attn_fwd_scaled(const void *Q, const void *K, const void *V, void *O, float *LSE,
+TSD_API int attn_fwd_scaled(const void *Q, const void *K, const void *V, void *O, float *LSE,
                     const float *Q_scale, const float *K_scale,
                     int64_t B, int64_t H, int64_t S_q, int64_t S_k,
                     int64_t D_qk, int64_t D_v, int64_t q_block, int64_t k_block,
                     int causal, int qk_dtype, int dtype, void *stream);
 
 /* attn_status_string — static text for a status code (never NULL). */
-const char *attn_status_string(int status);
+TSD_API const char *attn_status_string(int status);
 
 #ifdef __cplusplus
 }

@@ -49,6 +49,8 @@ def test_library_exports_every_declared_symbol(lib):
     exported = set(re.findall(r"\sT\s+(\w+)$", out, flags=re.M))
     for name in declared_functions():
         assert name in exported, f"{name} not exported"
+    # nothing else: the internals are built with hidden visibility
+    assert exported == set(declared_functions()), sorted(exported - set(declared_functions()))
 
 
 def test_status_strings(lib):

@@ -13,7 +13,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libtsd_attn.so")
-SOURCES = ["attn_api.hip", "attn_kernels.hip"]
+# (source, object name, extra defines): the kernel file is compiled once per
+# unit (plain + merge, extended, per-block scaled) so the units build in
+# parallel.
+SOURCES = [
+    ("attn_api.hip", "attn_api.o", []),
+    ("attn_kernels.hip", "attn_kernels_plain.o", ["-DTSD_UNIT=0"]),
+    ("attn_kernels.hip", "attn_kernels_ext.o", ["-DTSD_UNIT=1"]),
+    ("attn_kernels.hip", "attn_kernels_scaled.o", ["-DTSD_UNIT=2"]),
+]
 ARCH = "gfx950"
 
 # Packed-f32 VALU instructions are disabled for all device code.
@@ -21,6 +29,7 @@ HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
+    "-fvisibility=hidden",   # only the TSD_API entry points are exported
 ]
 
 
@@ -38,13 +47,14 @@ def build(output: str = LIBRARY, extra_flags=None, verbose: bool = False) -> str
     os.makedirs(tmpdir, exist_ok=True)
     flags = HIPCC_FLAGS + list(extra_flags or [])
     procs = []
-    for src in SOURCES:
-        obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
-        cmd = [hipcc(), *flags, "-I", INCLUDE, "-I", CSRC, "-c",
+    for src, obj_name, defines in SOURCES:
+        obj = os.path.join(tmpdir, obj_name)
+        cmd = [hipcc(), *flags, *defines, "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT), src))
+        procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT),
+                      obj_name))
         objs.append(obj)
     failed = []
     for proc, src in procs:

@@ -35,6 +35,13 @@
 
 #include "launch.h"
 
+// This file is compiled once per unit, each unit instantiating one family
+// of kernels so that the units build in parallel: 0 = the plain kernels and
+// the merge, 1 = the extended kernels, 2 = the per-block scaled kernels.
+#ifndef TSD_UNIT
+#define TSD_UNIT 0
+#endif
+
 namespace tsd {
 namespace {
 
@@ -1557,6 +1564,7 @@ hipError_t dispatch_causal(int dtype, bool causal, int64_t grid, const KernelArg
 
 }  // namespace
 
+#if TSD_UNIT == 0
 TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec)
 {
     TileConfig t;
@@ -1586,6 +1594,9 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec)
     return t;
 }
 
+#endif
+
+#if TSD_UNIT == 1
 hipError_t launch_attn_ext(const TileConfig &cfg, int dtype, bool causal, bool out_f32,
                            int64_t grid, const KernelArgs &args, hipStream_t stream)
 {
@@ -1598,6 +1609,9 @@ hipError_t launch_attn_ext(const TileConfig &cfg, int dtype, bool causal, bool o
     }
 }
 
+#endif
+
+#if TSD_UNIT == 2
 hipError_t launch_attn_scaled(const TileConfig &cfg, int dtype, bool causal, bool qk8,
                               int64_t grid, const KernelArgs &args, hipStream_t stream)
 {
@@ -1610,6 +1624,9 @@ hipError_t launch_attn_scaled(const TileConfig &cfg, int dtype, bool causal, boo
     }
 }
 
+#endif
+
+#if TSD_UNIT == 0
 hipError_t launch_merge(int dtype, bool vec, const MergeArgs &args, hipStream_t stream)
 {
     const int64_t threads = args.rows * args.groups;
@@ -1644,5 +1661,7 @@ hipError_t launch_attn(const TileConfig &cfg, int dtype, bool causal, int64_t gr
     default: return dispatch_causal<128, 128>(dtype, causal, grid, args, stream);
     }
 }
+
+#endif
 
 }  // namespace tsd
