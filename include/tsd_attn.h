@@ -102,9 +102,9 @@ typedef struct tsd_plan {
  * entries of LSE, are written.  Returns a TSD_* status.
  */
 TSD_API int attn_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
-             int64_t B, int64_t H, int64_t S_q, int64_t S_k,
-             int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
-             void *stream);
+                     int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                     int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+                     void *stream);
 
 /*
  * attn_fwd_plan — fill `out` with the plan attn_fwd would use for these
@@ -113,8 +113,8 @@ TSD_API int attn_fwd(const void *Q, const void *K, const void *V, void *O, float
  * same shape/dtype statuses as attn_fwd (TSD_ERR_NULL if out is NULL).
  */
 TSD_API int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
-                  int64_t D_qk, int64_t D_v, int causal, int dtype,
-                  tsd_plan *out);
+                          int64_t D_qk, int64_t D_v, int causal, int dtype,
+                          tsd_plan *out);
 
 /*
  * attn_fwd_plan_block — for workgroup `block` (0 <= block < plan->grid),
@@ -123,8 +123,8 @@ TSD_API int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
  * Returns TSD_ERR_SHAPE if `block` is out of range.
  */
 TSD_API int attn_fwd_plan_block(const tsd_plan *plan, int64_t S_q, int64_t S_k,
-                        int64_t block, int64_t *q_block, int64_t *slice,
-                        int64_t *kv_steps);
+                                int64_t block, int64_t *q_block, int64_t *slice,
+                                int64_t *kv_steps);
 
 /*
  * ------------------------------------------------------------------------
@@ -176,14 +176,16 @@ typedef struct tsd_mask {
 } tsd_mask;
 
 /*
- * attn_fwd_ext — attn_fwd with the visibility of `mask`.  O [B,H,S_q,D_v]
- * of `dtype`, LSE [B,H,S_q] f32 (may be NULL).  Same statuses as attn_fwd,
- * plus the mask and fast-path conditions above.
+ * attn_fwd_ext — attn_fwd with the visibility of `mask` and H_kv K/V heads
+ * (H_kv = H: the layout of attn_fwd).  Q [B,H,S_q,D_qk], K [B,H_kv,S_k,D_qk],
+ * V [B,H_kv,S_k,D_v]; O [B,H,S_q,D_v] of `dtype`, LSE [B,H,S_q] f32 (may be
+ * NULL).  Same statuses as attn_fwd, plus the mask, grouped-head and
+ * fast-path conditions above.
  */
 TSD_API int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, float *LSE,
-                 int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
-                 int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
-                 const tsd_mask *mask, void *stream);
+                         int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
+                         int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+                         const tsd_mask *mask, void *stream);
 
 /*
  * attn_fwd_partial — one partial result per key chunk (VeriTile proof
@@ -195,16 +197,18 @@ TSD_API int attn_fwd_ext(const void *Q, const void *K, const void *V, void *O, f
  *             the chunk's visible keys times V (0 if none);
  *   LSE_parts [n_splits,B,H,S_q] f32 (required): ln of the chunk's sum of
  *             exp of the scaled scores (-infinity if none).
- * split_len >= 1; a multiple of 64 keeps chunks on whole key tiles.
+ * Q, K, V and H_kv as for attn_fwd_ext.  n_splits >= 1 and split_len >= 1
+ * (TSD_ERR_SHAPE); kv_begin + n_splits * split_len must fit in int32
+ * (TSD_ERR_UNSUPPORTED); a multiple of 64 keeps chunks on whole key tiles.
  * Merging the n_splits results with attn_merge gives attn_fwd_ext's result
  * up to rounding.
  */
 TSD_API int attn_fwd_partial(const void *Q, const void *K, const void *V,
-                     float *O_parts, float *LSE_parts,
-                     int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
-                     int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
-                     const tsd_mask *mask, int64_t n_splits, int64_t split_len,
-                     void *stream);
+                             float *O_parts, float *LSE_parts,
+                             int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
+                             int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+                             const tsd_mask *mask, int64_t n_splits, int64_t split_len,
+                             void *stream);
 
 /*
  * attn_merge — combine n_parts partial results of the same rows (VeriTile
@@ -220,23 +224,24 @@ TSD_API int attn_fwd_partial(const void *Q, const void *K, const void *V,
  * the parts (TSD_ERR_ALIAS).
  */
 TSD_API int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_parts,
-               int64_t B, int64_t H, int64_t S_q, int64_t D_v,
-               void *O, float *LSE, int dtype, void *stream);
+                       int64_t B, int64_t H, int64_t S_q, int64_t D_v,
+                       void *O, float *LSE, int dtype, void *stream);
 
 /*
  * attn_splitkv_plan — the chunking attn_fwd_splitkv uses (host only).
  * n_splits <= 0 lets the library choose: enough chunks that one round of
  * workgroups covers the 256 compute units, chunks of at least 512 keys,
  * at most 256 chunks.  Reports the chunk count actually used (chunks are
- * whole 64-key tiles, so it may come out below the request), the chunk
- * length in keys and the workspace bytes attn_fwd_splitkv needs (0 when a
- * single chunk is used: then no workspace is touched).
+ * whole 64-key tiles, so it may come out below the request; a request
+ * above 256 is TSD_ERR_UNSUPPORTED), the chunk length in keys and the
+ * workspace bytes attn_fwd_splitkv needs (0 when a single chunk is used:
+ * then no workspace is touched).
  */
 TSD_API int attn_splitkv_plan(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
-                      int64_t D_qk, int64_t D_v, int causal, int dtype,
-                      const tsd_mask *mask, int64_t n_splits,
-                      int64_t *splits_out, int64_t *split_len_out,
-                      int64_t *workspace_bytes);
+                              int64_t D_qk, int64_t D_v, int causal, int dtype,
+                              const tsd_mask *mask, int64_t n_splits,
+                              int64_t *splits_out, int64_t *split_len_out,
+                              int64_t *workspace_bytes);
 
 /*
  * attn_fwd_splitkv — attn_fwd_ext computed as attn_fwd_partial over key
@@ -249,10 +254,10 @@ TSD_API int attn_splitkv_plan(int64_t B, int64_t H, int64_t H_kv, int64_t S_q, i
  * none.  Too small a workspace: TSD_ERR_SHAPE.
  */
 TSD_API int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
-                     int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
-                     int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
-                     const tsd_mask *mask, int64_t n_splits,
-                     void *workspace, int64_t workspace_bytes, void *stream);
+                             int64_t B, int64_t H, int64_t H_kv, int64_t S_q, int64_t S_k,
+                             int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
+                             const tsd_mask *mask, int64_t n_splits,
+                             void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
  * attn_fwd_scaled — base-2 attention with per-block Q and K scales
@@ -281,10 +286,10 @@ TSD_API int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *
  * Statuses, ownership and threading as for attn_fwd.
  */
 TSD_API int attn_fwd_scaled(const void *Q, const void *K, const void *V, void *O, float *LSE,
-                    const float *Q_scale, const float *K_scale,
-                    int64_t B, int64_t H, int64_t S_q, int64_t S_k,
-                    int64_t D_qk, int64_t D_v, int64_t q_block, int64_t k_block,
-                    int causal, int qk_dtype, int dtype, void *stream);
+                            const float *Q_scale, const float *K_scale,
+                            int64_t B, int64_t H, int64_t S_q, int64_t S_k,
+                            int64_t D_qk, int64_t D_v, int64_t q_block, int64_t k_block,
+                            int causal, int qk_dtype, int dtype, void *stream);
 
 /* attn_status_string — static text for a status code (never NULL). */
 TSD_API const char *attn_status_string(int status);
