@@ -10,11 +10,19 @@
 // exp(m_old - m_new) whenever m grows, which in real arithmetic gives the
 // plain definition exactly.
 //
-// Work decomposition (one workgroup = one query block of one slice):
-//   * 4 waves x 32 query rows = 128 rows per workgroup.
-//   * Each wave keeps its 32 query rows in VGPRs for the whole key loop.
-//   * Key/value tiles are staged through LDS, double buffered: the global
-//     loads of tile t+1 are in flight while tile t is computed.
+// Kernels in this file:
+//   * attn_fwd_fast16 — the main kernel: 16-bit inputs whose rows are
+//     16-byte aligned; plus its extended (key ranges, offsets, windows, key
+//     chunks, grouped heads), per-block scaled and fp8-score forms.
+//   * attn_fwd_16 / attn_fwd_32 — generic kernels for any alignment and
+//     head width (16-bit and f32 inputs), staged through VGPRs.
+//   * attn_merge_kernel — the merge of partial results over key chunks.
+//
+// Common work decomposition (one workgroup = one query block of one slice):
+//   * Each wave owns 32 query rows and keeps them in VGPRs for the whole
+//     key loop (the generic kernels: 4 waves, 128 rows per workgroup).
+//   * Key/value tiles are staged through LDS with their global loads in
+//     flight while earlier tiles are computed.
 //   * Scores are formed transposed, S^T = K Q^T, on MFMA: the 32x32 result
 //     puts one query per lane column, so each lane holds 16 keys of a single
 //     query and the row max / sum are in-lane plus one swap with lane^32.
@@ -666,16 +674,16 @@ attn_fwd_32(KernelArgs p)
 // ====================================================================
 // Fast 16-bit kernel (vector-aligned inputs, D_qk and D_v multiples of 8).
 //
-//   * 4 waves x 32 query rows = 128 rows per workgroup, two workgroups per
-//     CU (2 waves per SIMD from different workgroups, so their barriers do
-//     not lock the two waves of a SIMD into the same phase).
+//   * 32 query rows per wave; 8 waves (256 rows) per workgroup and one
+//     workgroup per CU for 128-wide heads, 4 waves and three workgroups per
+//     CU for 64-wide heads (FastShape below).
 //   * K and V tiles (64 keys) go HBM -> LDS directly with buffer loads
 //     (buffer_load_dwordx4 ... lds): no VGPR staging, no LDS write
 //     instructions.  The buffer range is the slice, so key rows >= S_k read
 //     as zero; head-dim chunks >= D read as zero through an out-of-range
-//     offset.  K and V have two LDS slots each (64 KB at D = 128): a tile's
-//     K is read one iteration before its V, so K is fetched two tiles ahead
-//     and V one tile ahead.
+//     offset.  K and V sit in LDS rings (4 and 2 tiles for 128-wide heads):
+//     a tile's K is read one iteration before its V, so K is fetched up to
+//     KS-1 tiles ahead and V VS-1 tiles ahead.
 //   * Each wave instruction fills 1 KB of LDS contiguously (lane i -> bytes
 //     16i..16i+15); the swizzle is realised by choosing which global chunk
 //     each lane fetches.
