@@ -50,7 +50,7 @@ def test_counter_mean_over_matching_dispatches(tmp_path):
 
 def test_record_and_lookup_traffic(tmp_path, monkeypatch):
     src = tmp_path / "kernels.hip"
-    src.write_text("// kernel source v1\n")
+    src.write_text("int v = 1; // kernel source v1\n")
     traffic = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(traffic))
@@ -70,7 +70,9 @@ def test_record_and_lookup_traffic(tmp_path, monkeypatch):
     assert rec["read_bytes"] == 2 * 1000 * 1024
     assert rec["write_bytes"] == 250 * 1024
     assert bench.stored_traffic("bf16_b1h32_s16384_d128_causal") == 2 * 1000 * 1024 + 250 * 1024
-    # a changed kernel source invalidates the record
-    src.write_text("// kernel source v2\n")
+    # an edit of comments only keeps the record; a changed kernel invalidates it
+    src.write_text("int v = 1;   // the same code, another comment\n")
+    assert bench.stored_traffic("bf16_b1h32_s16384_d128_causal") == 2 * 1000 * 1024 + 250 * 1024
+    src.write_text("int v = 2; // kernel source v2\n")
     assert bench.stored_traffic("bf16_b1h32_s16384_d128_causal") is None
     assert bench.stored_traffic("no_such_workload") is None
