@@ -80,6 +80,8 @@ typedef struct tsd_plan {
     int64_t grid;           /* workgroups launched = q_blocks * slices          */
     int64_t total_kv_steps; /* sum over workgroups of the key tiles visited     */
     int64_t vector_io;      /* 1: 16-byte global loads/stores; 0: per element   */
+    int64_t key_split;      /* waves of a workgroup that split its key tiles    */
+                            /* between them (f32 on small grids: 4), else 1     */
 } tsd_plan;
 
 /*

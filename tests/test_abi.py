@@ -147,7 +147,13 @@ def expected_tiles(qb, bm, bn, S_q, S_k, causal):
 def test_plan_for_workloads(lib, name):
     w = WORKLOADS[name]
     plan = tsd.attn_fwd_plan(w.B, w.H, w.S_q, w.S_k, w.D_qk, w.D_v, w.causal, w.dtype)
-    if w.dtype == "f32":
+    if w.dtype == "f32" and plan.key_split > 1:
+        # f32 on a small grid: 32 rows per workgroup, the 4 waves split the
+        # 32-key tiles (one LDS region each, combined at the end)
+        assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (32, 256, 4, 32)
+        assert plan.key_split == 4
+        assert plan.lds_bytes <= 160 * 1024
+    elif w.dtype == "f32":
         # generic kernel: 4 waves x 32 rows, 32-key tiles, two LDS stages
         assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (128, 256, 4, 32)
         assert plan.lds_bytes <= 64 * 1024
@@ -173,6 +179,25 @@ def test_plan_for_workloads(lib, name):
     total = sum(expected_tiles(qb, bm, plan.block_n, w.S_q, w.S_k, w.causal)
                 for qb in range(plan.q_blocks)) * plan.slices
     assert plan.total_kv_steps == total
+
+
+@pytest.mark.parametrize("B,H,S_q,D,split", [
+    (1, 2, 128, 64, 4),      # 2 slices x 1 block of 128 rows
+    (2, 4, 1000, 80, 4),     # 64 blocks of 128 rows
+    (1, 8, 2048, 128, 4),    # 128
+    (2, 16, 1920, 128, 4),   # 480: still below two per CU
+    (2, 16, 2048, 128, 1),   # 512: the 128-row kernel, two workgroups per CU
+    (4, 32, 4096, 64, 1),
+])
+def test_f32_key_split_choice(lib, B, H, S_q, D, split):
+    """f32 takes the key-split kernel (32 rows per workgroup) exactly when
+    the 128-row kernel would launch fewer than 512 workgroups; 16-bit inputs
+    never split."""
+    plan = tsd.attn_fwd_plan(B, H, S_q, 777, D, D, False, "f32")
+    assert plan.key_split == split
+    assert plan.block_m == (32 if split > 1 else 128)
+    assert plan.grid == math.ceil(S_q / plan.block_m) * B * H
+    assert tsd.attn_fwd_plan(B, H, S_q, 777, D, D, False, "bf16").key_split == 1
 
 
 @pytest.mark.parametrize("B,H,S_q,S_k,causal", [

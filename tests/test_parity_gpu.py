@@ -120,6 +120,31 @@ def test_edge_shapes(case, causal, dtype):
     check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"{case} c={causal} {dtype}")
 
 
+# ------------------------------------------------------ the two f32 kernels
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [
+    (2, 16, 2048, 1999, 80, 72),   # 512 blocks of 128 rows: the 128-row kernel
+    (2, 16, 1920, 2001, 80, 72),   # 480 such blocks: the key-split kernel
+])
+def test_f32_kernels_on_large_grids(shape, causal):
+    """f32 just above and just below the switch to the key-split kernel (32
+    rows per workgroup, the waves splitting the key tiles), a row sample on
+    both sides of every block boundary against the oracle."""
+    B, H, S_q, S_k, D_qk, D_v = shape
+    plan = tsd.attn_fwd_plan(B, H, S_q, S_k, D_qk, D_v, causal, "f32")
+    assert plan.key_split == (1 if S_q == 2048 else 4)
+    print(f"[case] f32 {shape} causal={causal} block_m={plan.block_m}", flush=True)
+    q, k, v = random_inputs((B, H, S_q, D_qk), (B, H, S_k, D_qk), (B, H, S_k, D_v), "f32",
+                            seed=5000 + S_q)
+    scale = 1 / math.sqrt(D_qk)
+    o, lse = run_gpu(q, k, v, scale, causal)
+    rows = sample_rows(S_q, block_m=plan.block_m)
+    o_s, lse_s = to_np(o[:, :, rows]), to_np(lse[:, :, rows])
+    del o, lse
+    o_ref, lse_ref = run_oracle(q, k, v, scale, causal, rows=rows)
+    check(o_s, lse_s, o_ref, lse_ref, "f32", f"f32 {shape} c={causal} ({len(rows)} rows/slice)")
+
+
 # ------------------------------------------- masked keys and the running max
 def _aligned_inputs(S_q, S_k, D, key_score, dtype, seed):
     """Q rows all equal to u = (1/8, ..., 1/8) and K row j = u * a_j, so that

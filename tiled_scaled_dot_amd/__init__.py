@@ -59,6 +59,7 @@ class TsdPlan(ctypes.Structure):
         ("grid", ctypes.c_int64),
         ("total_kv_steps", ctypes.c_int64),
         ("vector_io", ctypes.c_int64),
+        ("key_split", ctypes.c_int64),
     ]
 
     def as_dict(self):

@@ -56,7 +56,7 @@ int check_shape(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, in
 void fill_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
                int causal, int dtype, bool vector_io, tsd_plan *pl)
 {
-    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, vector_io);
+    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, vector_io, B * H, S_q);
     std::memset(pl, 0, sizeof(*pl));
     pl->dtype = dtype;
     pl->causal = causal ? 1 : 0;
@@ -73,6 +73,7 @@ void fill_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int
     pl->grid = pl->q_blocks * pl->slices;
     pl->order = (pl->slices % 8 == 0) ? 1 : 0;
     pl->vector_io = vector_io ? 1 : 0;
+    pl->key_split = cfg.split_keys ? cfg.waves : 1;
     int64_t steps = 0;
     for (int64_t qb = 0; qb < pl->q_blocks; ++qb)
         steps += tsd::kv_tiles_for((int32_t)qb, cfg.block_m, cfg.block_n, (int32_t)S_q,
@@ -316,7 +317,7 @@ extern "C" int attn_fwd(const void *Q, const void *K, const void *V, void *O, fl
     const tsd::KernelArgs a =
         base_args(Q, K, V, O, LSE, S_q, S_k, D_qk, D_v, scale, dtype, vec, plan);
 
-    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, vec);
+    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, vec, B * H, S_q);
     hipError_t err = tsd::launch_attn(cfg, dtype, causal != 0, plan.grid, a,
                                       reinterpret_cast<hipStream_t>(stream));
     return err == hipSuccess ? TSD_OK : TSD_ERR_HIP;

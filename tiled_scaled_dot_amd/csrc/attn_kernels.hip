@@ -16,6 +16,8 @@
 //     chunks, grouped heads), per-block scaled and fp8-score forms.
 //   * attn_fwd_16 / attn_fwd_32 — generic kernels for any alignment and
 //     head width (16-bit and f32 inputs), staged through VGPRs.
+//   * attn_fwd_32s — f32 on small grids: 32 rows per workgroup, the four
+//     waves splitting the key tiles, combined through LDS at the end.
 //   * attn_merge_kernel — the merge of partial results over key chunks.
 //
 // Common work decomposition (one workgroup = one query block of one slice):
@@ -742,7 +744,7 @@ using IC = std::integral_constant<int, N>;
 
 // f(IC<B>{}), f(IC<B+1>{}), ..., f(IC<E-1>{})
 template <int B, int E, typename F>
-__device__ __attribute__((always_inline)) inline void static_for(F &&f)
+__host__ __device__ __attribute__((always_inline)) inline void static_for(F &&f)
 {
     if constexpr (B < E) {
         f(IC<B>{});
@@ -1388,7 +1390,325 @@ attn_fwd_fast16(KernelArgs p)
     }
 }
 
+// ====================================================================
+// f32 kernel with the key tiles split over the waves, for small grids.
+//
+// When 128-row workgroups would leave most CUs idle (few slices, short
+// sequences), a workgroup takes 32 query rows and its four waves (one per
+// SIMD) split the key tiles: wave w takes tiles w, w+4, w+8, ..., each with
+// its own online softmax over the keys it sees.  The four partial results
+// (running max m_w, sum l_w, unnormalised O_w) are combined through LDS at
+// the end, as chunks of keys are merged: M = max m_w, a_w = exp(m_w - M),
+// O = sum a_w O_w / sum a_w l_w.
+//
+// A wave stages its own tiles in a private LDS region (K at 16-byte chunk
+// c ^ (row % 8) of its row, V row-major), so the key loop has no barrier.
+// One tile's worth of registers carries the loads in flight: K(t+4) is
+// loaded while the softmax and P V of tile t run and stored after them; V(t)
+// is loaded while the scores of t run and stored after them.
+// ====================================================================
+template <int DQ, int DV>
+struct Split32 {
+    static constexpr int BN = 32;                              // keys per tile
+    static constexpr int KCH = DQ / 4, VCH = DV / 4;           // 16-byte chunks per row
+    static constexpr int K_CHUNKS = BN * KCH, V_CHUNKS = BN * VCH;
+    static constexpr int K_PER_L = K_CHUNKS / 64, V_PER_L = V_CHUNKS / 64;   // per lane
+    static constexpr int REGS = K_PER_L > V_PER_L ? K_PER_L : V_PER_L;
+    static constexpr int WAVE_CHUNKS = K_CHUNKS + V_CHUNKS;   // LDS per wave
+    // combination: O_w as [wave][row][OROW] floats, then m_w and l_w [wave][row]
+    static constexpr int OROW = DV + 4;
+    static constexpr int COMBINE_CHUNKS = (4 * 32 * OROW + 2 * 4 * 32) / 4;
+    static constexpr int LDS_CHUNKS =
+        4 * WAVE_CHUNKS > COMBINE_CHUNKS ? 4 * WAVE_CHUNKS : COMBINE_CHUNKS;
+    static_assert(K_CHUNKS % 64 == 0 && V_CHUNKS % 64 == 0 && KCH % 8 == 0, "tile split");
+};
+constexpr int kSplitRows = 32;   // query rows per workgroup of the split kernel
+
+
+template <int DQ, int DV, bool CAUSAL>
+__global__ void __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                               amdgpu_waves_per_eu(1, 1)))
+attn_fwd_32s(KernelArgs p)
+{
+    using T = Split32<DQ, DV>;
+    constexpr int BN = T::BN;
+    __shared__ u32x4 lds[T::LDS_CHUNKS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int hh = lane >> 5, l32 = lane & 31;
+
+    int32_t qb, slice;
+    map_block((int32_t)blockIdx.x, p.q_blocks, p.slices, p.order, p.per_xcd, CAUSAL, qb, slice);
+    // workgroup-uniform: keeps the buffer descriptors below in scalar registers
+    qb = __builtin_amdgcn_readfirstlane(qb);
+    slice = __builtin_amdgcn_readfirstlane(slice);
+    const int q0 = qb * kSplitRows;
+    const int qi = q0 + l32;
+
+    // Buffer descriptors over this slice's Q, K and V: an offset past the
+    // slice reads as zero, so rows past S_q / S_k and columns past D need no
+    // branch (offsets are 32-bit: a slice is below 2^31 bytes).
+    const uint32_t q_bytes = (uint32_t)p.S_q * p.D_qk * 4;
+    const uint32_t k_bytes = (uint32_t)p.S_k * p.D_qk * 4;
+    const uint32_t v_bytes = (uint32_t)p.S_k * p.D_v * 4;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(static_cast<const uint8_t *>(p.Q) + (size_t)slice * q_bytes, q_bytes);
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(static_cast<const uint8_t *>(p.K) + (size_t)slice * k_bytes, k_bytes);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(static_cast<const uint8_t *>(p.V) + (size_t)slice * v_bytes, v_bytes);
+    // Columns col .. col+3 of a row of a row-major f32 matrix with `ncols`
+    // columns; zero past nrows rows or ncols columns: one 16-byte load when
+    // the inputs are vector-aligned (ncols % 4 == 0), else four 4-byte loads.
+    auto load4v = [&](__amdgpu_buffer_rsrc_t r, int row, int nrows, int col, int ncols)
+        __attribute__((always_inline)) {
+        const uint32_t off =
+            (row < nrows && col < ncols) ? (uint32_t)(row * ncols + col) * 4 : kOutOfRange;
+        return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    };
+    auto load4s = [&](__amdgpu_buffer_rsrc_t r, int row, int nrows, int col, int ncols)
+        __attribute__((always_inline)) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t off = (row < nrows && col + e < ncols)
+                                     ? (uint32_t)(row * ncols + col + e) * 4
+                                     : kOutOfRange;
+            w[e] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+        }
+        return u32x4{w[0], w[1], w[2], w[3]};
+    };
+
+    // Q fragment: step 4u+j of the k=2 MFMA uses dim 8u + 4hh + j.
+    float qf[DQ / 2];
+#pragma unroll
+    for (int u = 0; u < DQ / 8; ++u) {
+        u32x4 x = p.vec ? load4v(rq, qi, p.S_q, u * 8 + hh * 4, p.D_qk)
+                        : load4s(rq, qi, p.S_q, u * 8 + hh * 4, p.D_qk);
+        x = (x ^ p.q_xor) & p.q_and;
+        const f32x4 xf = __builtin_bit_cast(f32x4, x);   // whole-vector bit cast
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qf[4 * u + j] = xf[j];
+    }
+
+    const int ntiles = kv_tiles_for(qb, kSplitRows, BN, p.S_q, p.S_k, CAUSAL);
+    const float c = p.c;
+
+    f32x16 o[DV / 32];
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d) o[d] = f32x16{};
+    float m = neg_inf();
+    float l = 0.0f;
+
+    u32x4 *Kw = lds + wave * T::WAVE_CHUNKS;   // this wave's K tile, then its V tile
+    const float *Vw = reinterpret_cast<const float *>(Kw + T::K_CHUNKS);
+    u32x4 rg[T::REGS];
+    auto load_k = [&](int t) __attribute__((always_inline)) {
+        if (p.vec) {
+#pragma unroll
+            for (int it = 0; it < T::K_PER_L; ++it) {
+                const int ci = lane + 64 * it;
+                rg[it] = load4v(rk, t * BN + ci / T::KCH, p.S_k, (ci % T::KCH) * 4, p.D_qk);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < T::K_PER_L; ++it) {
+                const int ci = lane + 64 * it;
+                rg[it] = load4s(rk, t * BN + ci / T::KCH, p.S_k, (ci % T::KCH) * 4, p.D_qk);
+            }
+        }
+    };
+    auto store_k = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < T::K_PER_L; ++it) {
+            const int ci = lane + 64 * it;
+            const int row = ci / T::KCH, cc = ci % T::KCH;
+            Kw[row * T::KCH + (cc ^ (row & 7))] = rg[it];
+        }
+    };
+    auto load_v = [&](int t) __attribute__((always_inline)) {
+        if (p.vec) {
+#pragma unroll
+            for (int it = 0; it < T::V_PER_L; ++it) {
+                const int ci = lane + 64 * it;
+                rg[it] = load4v(rv, t * BN + ci / T::VCH, p.S_k, (ci % T::VCH) * 4, p.D_v);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < T::V_PER_L; ++it) {
+                const int ci = lane + 64 * it;
+                rg[it] = load4s(rv, t * BN + ci / T::VCH, p.S_k, (ci % T::VCH) * 4, p.D_v);
+            }
+        }
+    };
+    auto store_v = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int it = 0; it < T::V_PER_L; ++it) Kw[T::K_CHUNKS + lane + 64 * it] = rg[it];
+    };
+
+    // LDS reads and writes of one wave execute in order, so a region is
+    // rewritten only after the reads of the tile before have been served.
+    if (wave < ntiles) {
+        load_k(wave);
+        store_k();
+        load_v(wave);
+    }
+    for (int t = wave; t < ntiles; t += 4) {
+        const int kbase = t * BN;
+
+        // ---- S^T: lane (l32, hh) gets keys (r/4)*8 + 4hh + r%4 of query qi
+        // Operand reads run ahead of the MFMAs that use them (three K chunks,
+        // two V keys); scheduling barriers keep the compiler from sinking
+        // them back next to their use.
+        f32x16 s = f32x16{};
+        {
+            constexpr int NU = DQ / 8;
+            f32x4 ka[4];
+            auto kread = [&](int u) __attribute__((always_inline)) {
+                return __builtin_bit_cast(f32x4, Kw[l32 * T::KCH + ((2 * u + hh) ^ (l32 & 7))]);
+            };
+#pragma unroll
+            for (int u = 0; u < 3; ++u) ka[u] = kread(u);
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (u + 3 < NU) ka[(u + 3) & 3] = kread(u + 3);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s = mma32(ka[u & 3][j], qf[4 * u + j], s);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        store_v();                               // V(t): the P V of tile t-4 is done
+        if (t + 4 < ntiles) load_k(t + 4);
+
+        const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > q0);
+        if (need_mask) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kbase + (r >> 2) * 8 + hh * 4 + (r & 3);
+                bool ok = key < p.S_k;
+                if (CAUSAL) ok = ok && key <= qi;
+                s[r] = ok ? s[r] : neg_inf();
+            }
+        }
+
+        // Every tile a wave visits holds a key visible to each of its rows
+        // (key kbase <= the first row when causal, kbase < S_k), so m is
+        // finite from the first tile on.  The running max only moves when
+        // some row's max grows by more than 2^kTau in the exponent (always on
+        // the first tile), so O and l are rescaled rarely and P stays
+        // below 2^kTau.
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = fmaxf(mx, other_half(mx));
+        if (__builtin_amdgcn_ballot_w64((mx - m) * c > kTau) != 0) {
+            const float m_new = fmaxf(m, mx);
+            const float alpha = fast_exp2((m - m_new) * c);
+            m = m_new;
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+        }
+        const float mc = m * c;
+
+        float pv[16];
+        float rs = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            pv[r] = fast_exp2(__builtin_fmaf(s[r], c, -mc));
+            rs += pv[r];
+        }
+        l += rs;
+
+        // ---- O^T += V^T P^T; step r uses key (r/4)*8 + 4hh + r%4
+        {
+            float va[3][DV / 32];
+            auto vread = [&](int r, float (&dst)[DV / 32]) __attribute__((always_inline)) {
+                const int key = (r >> 2) * 8 + hh * 4 + (r & 3);
+#pragma unroll
+                for (int d = 0; d < DV / 32; ++d) dst[d] = Vw[key * DV + d * 32 + l32];
+            };
+            vread(0, va[0]);
+            vread(1, va[1]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                if (r + 2 < 16) vread(r + 2, va[(r + 2) % 3]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int d = 0; d < DV / 32; ++d) o[d] = mma32(va[r % 3][d], pv[r], o[d]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+
+        if (t + 4 < ntiles) {
+            store_k();                           // K(t+4): the scores of t are done
+            load_v(t + 4);
+        }
+    }
+
+    // ---- combination of the four waves' partial results
+    __syncthreads();   // every wave is done with its K / V region
+    float *cmb = reinterpret_cast<float *>(lds);
+    float *cm = cmb + 4 * 32 * T::OROW;   // m_w per row
+    float *cl = cm + 4 * 32;              // l_w per row (both lane halves)
+    const float lt = l + other_half(l);
+#pragma unroll
+    for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int d0 = d * 32 + g * 8 + hh * 4;
+            *reinterpret_cast<f32x4 *>(cmb + (wave * 32 + l32) * T::OROW + d0) =
+                f32x4{o[d][4 * g], o[d][4 * g + 1], o[d][4 * g + 2], o[d][4 * g + 3]};
+        }
+    if (hh == 0) {
+        cm[wave * 32 + l32] = m;   // -inf for a wave without tiles (its l and O are 0)
+        cl[wave * 32 + l32] = lt;
+    }
+    __syncthreads();
+
+    // thread (row r, part) writes columns 4 * (part + 8 i) .. +3 of row q0 + r
+    const int r = tid >> 3, part = tid & 7;
+    float mw[4], mmax = neg_inf();
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        mw[w] = cm[w * 32 + r];
+        mmax = fmaxf(mmax, mw[w]);
+    }
+    float aw[4], lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        aw[w] = fast_exp2((mw[w] - mmax) * c);   // 0 for a wave without tiles
+        lsum += aw[w] * cl[w * 32 + r];
+    }
+    const float inv = 1.0f / lsum;
+    const int row = q0 + r;
+    if (row < p.S_q) {
+        float *Os = static_cast<float *>(p.O) + ((size_t)slice * p.S_q + row) * p.D_v;
+#pragma unroll
+        for (int i = 0; i < DV / 32; ++i) {
+            const int d0 = 4 * (part + 8 * i);
+            f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                acc += aw[w] * *reinterpret_cast<const f32x4 *>(cmb + (w * 32 + r) * T::OROW + d0);
+            acc *= inv;
+            if (p.vec) {
+                if (d0 < p.D_v) *reinterpret_cast<f32x4 *>(Os + d0) = acc;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (d0 + j < p.D_v) Os[d0 + j] = acc[j];
+            }
+        }
+        if (p.LSE && part == 0)
+            p.LSE[(size_t)slice * p.S_q + row] = (mmax * c + __builtin_amdgcn_logf(lsum)) * kLn2;
+    }
+}
+
 int pad_dim(int64_t d) { return d <= 64 ? 64 : 128; }
+int pad_split(int64_t d) { return d <= 64 ? 64 : d <= 96 ? 96 : 128; }
 
 template <typename Kern>
 hipError_t launch(Kern kern, int64_t grid, const KernelArgs &args, hipStream_t stream,
@@ -1561,6 +1881,13 @@ __global__ void __launch_bounds__(kMergeThreads) attn_merge_kernel(MergeArgs p)
 }
 
 template <int DQ, int DV>
+hipError_t dispatch_split(bool causal, int64_t grid, const KernelArgs &a, hipStream_t s)
+{
+    return causal ? launch(attn_fwd_32s<DQ, DV, true>, grid, a, s)
+                  : launch(attn_fwd_32s<DQ, DV, false>, grid, a, s);
+}
+
+template <int DQ, int DV>
 hipError_t dispatch_causal(int dtype, bool causal, int64_t grid, const KernelArgs &a,
                            hipStream_t s)
 {
@@ -1577,12 +1904,21 @@ hipError_t dispatch_causal(int dtype, bool causal, int64_t grid, const KernelArg
 }  // namespace
 
 #if TSD_UNIT == 0
-TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec)
+#ifndef TSD_SPLIT_BELOW
+#define TSD_SPLIT_BELOW 512
+#endif
+TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec, int64_t slices,
+                       int64_t S_q)
 {
     TileConfig t;
     t.dqk_block = pad_dim(D_qk);
     t.dv_block = pad_dim(D_v);
     t.fast = dtype != TSD_F32 && vec;
+    // f32: the 128-row kernel runs two workgroups per CU; when it would
+    // launch fewer than two per CU, the key-split kernel (32 rows per
+    // workgroup) spreads the work over four times as many.
+    t.split_keys = dtype == TSD_F32 && slices > 0 &&
+                   slices * ((S_q + kBlockM - 1) / kBlockM) < TSD_SPLIT_BELOW;
     if (t.fast) {
         const FastShape sh = fast_shape(t.dqk_block, t.dv_block);
         t.block_m = 32 * sh.waves;
@@ -1590,6 +1926,20 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec)
         t.threads = 64 * sh.waves;
         t.block_n = 64;
         t.lds_bytes = (sh.kslots * t.dqk_block + sh.vslots * t.dv_block) * 64 * 2;
+    } else if (t.split_keys) {
+        // widths padded to 64, 96 or 128 (MFMA work grows with the padding)
+        t.dqk_block = pad_split(D_qk);
+        t.dv_block = pad_split(D_v);
+        t.block_m = kSplitRows;
+        t.waves = kThreads / 64;
+        t.threads = kThreads;
+        t.block_n = 32;
+        t.lds_bytes = 0;
+        static_for<0, 9>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int dq = 64 + 32 * (i / 3), dv = 64 + 32 * (i % 3);
+            if (t.dqk_block == dq && t.dv_block == dv) t.lds_bytes = 16 * Split32<dq, dv>::LDS_CHUNKS;
+        });
     } else if (dtype == TSD_F32) {
         t.block_m = kBlockM;
         t.waves = kThreads / 64;
@@ -1658,6 +2008,16 @@ hipError_t launch_attn(const TileConfig &cfg, int dtype, bool causal, int64_t gr
                        const KernelArgs &args, hipStream_t stream)
 {
     const int key = (cfg.dqk_block == 128 ? 2 : 0) + (cfg.dv_block == 128 ? 1 : 0);
+    if (cfg.split_keys) {
+        hipError_t err = hipErrorInvalidValue;
+        static_for<0, 9>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int dq = 64 + 32 * (i / 3), dv = 64 + 32 * (i % 3);
+            if (cfg.dqk_block == dq && cfg.dv_block == dv)
+                err = dispatch_split<dq, dv>(causal, grid, args, stream);
+        });
+        return err;
+    }
     if (cfg.fast) {
         switch (key) {
         case 0: return dispatch_fast<64, 64>(dtype, causal, grid, args, stream);

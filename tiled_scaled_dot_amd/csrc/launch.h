@@ -120,10 +120,14 @@ __host__ __device__ inline int32_t kv_tiles_for(int32_t q_block, int32_t block_m
 // and the launcher so both agree).
 struct TileConfig {
     int32_t block_m, block_n, waves, threads, dqk_block, dv_block, lds_bytes;
-    bool fast;   // 16-byte aligned 16-bit inputs: the LDS-direct kernel
+    bool fast;         // 16-byte aligned 16-bit inputs: the LDS-direct kernel
+    bool split_keys;   // f32 on a small grid: 32 rows per workgroup, the
+                       // waves splitting the key tiles
 };
 
-TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec);
+// `slices` and `S_q` size the grid (0: not known, no key split).
+TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec, int64_t slices = 0,
+                       int64_t S_q = 0);
 
 // Launch the kernel that matches (dtype, dqk_block, dv_block, causal).
 hipError_t launch_attn(const TileConfig &cfg, int dtype, bool causal, int64_t grid,
