@@ -767,6 +767,9 @@ __host__ __device__ __attribute__((always_inline)) inline void static_for(F &&f)
 #ifndef TSD_SCHED_LEAD
 #define TSD_SCHED_LEAD 4
 #endif
+#ifndef TSD_DMA_LEAD
+#define TSD_DMA_LEAD 1
+#endif
 #ifndef TSD_SCHED_VALU8
 #define TSD_SCHED_VALU8 4   // VALU slots per fp8 score MFMA, in units of TSD_SCHED_VALU
 #endif
@@ -816,11 +819,17 @@ struct Fast16 {
     static constexpr int KS = SH.kslots, VS = SH.vslots, U = SH.kslots;
     static constexpr int K_SLOT0 = 0, V_SLOT0 = KS * KT;
     static constexpr int LDS_BYTES = KS * KT + VS * VT;
-    static constexpr int K_PER_W = KT / 1024 / NW;   // 1 KB load instructions per wave
-    static constexpr int V_PER_W = VT / 1024 / NW;
-    static constexpr int LOADS = K_PER_W + V_PER_W;  // per wave per tile
-    static_assert(K_PER_W >= 1 && V_PER_W >= 1 && KT % (1024 * NW) == 0 &&
-                      VT % (1024 * NW) == 0, "tile split");
+    // Waves that issue the tile loads: with two waves per SIMD (waves w and
+    // w+4 share one), only the first of each pair.  It is the older one,
+    // ahead in issue priority, and reaches the barrier ~600 clocks before
+    // the second; this way the second starts its MFMAs right after the
+    // barrier instead of issuing loads.
+    static constexpr int DMA_WAVES = (TSD_DMA_LEAD && NW == 8) ? NW / 2 : NW;
+    static constexpr int K_PER_W = KT / 1024 / DMA_WAVES;   // 1 KB loads per issuing wave
+    static constexpr int V_PER_W = VT / 1024 / DMA_WAVES;
+    static constexpr int LOADS = K_PER_W + V_PER_W;  // per issuing wave per tile
+    static_assert(K_PER_W >= 1 && V_PER_W >= 1 && KT % (1024 * DMA_WAVES) == 0 &&
+                      VT % (1024 * DMA_WAVES) == 0, "tile split");
     static_assert(VS >= 2 && KS >= VS && KS % VS == 0 && (KS == 2 || KS == 4), "ring sizes");
     // ds_read immediate offsets are 16-bit: every K slot and every V slot
     // must be reachable from one base register each.
@@ -972,24 +981,27 @@ attn_fwd_fast16(KernelArgs p)
     const u32x4 rv = rsrc_words(static_cast<const uint8_t *>(p.V) + (size_t)slice * v_bytes, v_bytes);
 
     // ---- per-lane source offsets of this wave's K/V load instructions
+    // (waves past DMA_WAVES issue no loads; their offsets are those of wave 0)
+    const bool dma_wave = T::DMA_WAVES == T::NW || wave < T::DMA_WAVES;
+    const int dw = dma_wave ? wave : 0;
     uint32_t koff[T::K_PER_W], voff[T::V_PER_W];
 #pragma unroll
     for (int j = 0; j < T::K_PER_W; ++j) {
-        const int P = (wave * T::K_PER_W + j) * 64 + lane;   // chunk slot in the K tile
+        const int P = (dw * T::K_PER_W + j) * 64 + lane;   // chunk slot in the K tile
         const int row = P / T::KCH, c = (P % T::KCH) ^ kswz<T::KCH>(row);
         constexpr int EPC = 16 / QKB;   // elements per 16-byte chunk
         koff[j] = c * EPC < p.D_qk ? (uint32_t)(row * p.D_qk + c * EPC) * QKB : kOutOfRange;
     }
 #pragma unroll
     for (int j = 0; j < T::V_PER_W; ++j) {
-        const int P = (wave * T::V_PER_W + j) * 64 + lane;
+        const int P = (dw * T::V_PER_W + j) * 64 + lane;
         const int row = P / T::VCH, c = (P % T::VCH) ^ vswz<T::VCH>(row);
         voff[j] = c * 8 < p.D_v ? (uint32_t)(row * p.D_v + c * 8) * 2 : kOutOfRange;
     }
     const uint32_t lds_k0 = (uint32_t)__builtin_amdgcn_readfirstlane(
-        lds_address(smem) + T::K_SLOT0 + (uint32_t)wave * T::K_PER_W * 1024);
+        lds_address(smem) + T::K_SLOT0 + (uint32_t)dw * T::K_PER_W * 1024);
     const uint32_t lds_v0 = (uint32_t)__builtin_amdgcn_readfirstlane(
-        lds_address(smem) + T::V_SLOT0 + (uint32_t)wave * T::V_PER_W * 1024);
+        lds_address(smem) + T::V_SLOT0 + (uint32_t)dw * T::V_PER_W * 1024);
     // K(t) into K slot t % KS and V(t) into V slot t % VS; the slot is a
     // compile-time constant at every call.
     // The tile's offset moves the descriptor's base (and shrinks its range)
@@ -998,14 +1010,18 @@ attn_fwd_fast16(KernelArgs p)
     auto issue_k = [&](int t, auto slot_c) __attribute__((always_inline)) {
         constexpr uint32_t sl = decltype(slot_c)::value * T::KT;
         const u32x4 r = tile_rsrc(rk, (uint32_t)(t_first + t) * BN * p.D_qk * QKB);
+        if (dma_wave) {
 #pragma unroll
-        for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + sl + j * 1024, koff[j], r);
+            for (int j = 0; j < T::K_PER_W; ++j) dma16(lds_k0 + sl + j * 1024, koff[j], r);
+        }
     };
     auto issue_v = [&](int t, auto slot_c) __attribute__((always_inline)) {
         constexpr uint32_t sl = decltype(slot_c)::value * T::VT;
         const u32x4 r = tile_rsrc(rv, (uint32_t)(t_first + t) * BN * p.D_v * 2);
+        if (dma_wave) {
 #pragma unroll
-        for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + sl + j * 1024, voff[j], r);
+            for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + sl + j * 1024, voff[j], r);
+        }
     };
 
     // Output of this slice (of chunk `split` when the output is partial).
