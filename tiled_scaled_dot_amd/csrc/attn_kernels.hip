@@ -1429,7 +1429,6 @@ struct Split32 {
     static constexpr int KCH = DQ / 4, VCH = DV / 4;           // 16-byte chunks per row
     static constexpr int K_CHUNKS = BN * KCH, V_CHUNKS = BN * VCH;
     static constexpr int K_PER_L = K_CHUNKS / 64, V_PER_L = V_CHUNKS / 64;   // per lane
-    static constexpr int REGS = K_PER_L > V_PER_L ? K_PER_L : V_PER_L;
     static constexpr int WAVE_CHUNKS = K_CHUNKS + V_CHUNKS;   // LDS per wave
     // combination: O_w as [wave][row][OROW] floats, then m_w and l_w [wave][row]
     static constexpr int OROW = DV + 4;
@@ -1451,7 +1450,8 @@ attn_fwd_32s(KernelArgs p)
     __shared__ u32x4 lds[T::LDS_CHUNKS];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, l32 = lane & 31;
 
     int32_t qb, slice;
@@ -1519,150 +1519,150 @@ attn_fwd_32s(KernelArgs p)
 
     u32x4 *Kw = lds + wave * T::WAVE_CHUNKS;   // this wave's K tile, then its V tile
     const float *Vw = reinterpret_cast<const float *>(Kw + T::K_CHUNKS);
-    u32x4 rg[T::REGS];
-    auto load_k = [&](int t) __attribute__((always_inline)) {
-        if (p.vec) {
-#pragma unroll
-            for (int it = 0; it < T::K_PER_L; ++it) {
-                const int ci = lane + 64 * it;
-                rg[it] = load4v(rk, t * BN + ci / T::KCH, p.S_k, (ci % T::KCH) * 4, p.D_qk);
-            }
-        } else {
-#pragma unroll
-            for (int it = 0; it < T::K_PER_L; ++it) {
-                const int ci = lane + 64 * it;
-                rg[it] = load4s(rk, t * BN + ci / T::KCH, p.S_k, (ci % T::KCH) * 4, p.D_qk);
-            }
-        }
-    };
-    auto store_k = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int it = 0; it < T::K_PER_L; ++it) {
-            const int ci = lane + 64 * it;
+
+    // The key loop, for 16-byte (VEC) or 4-byte global loads.  Per tile t:
+    // the scores of t, during which V(t) goes from registers to LDS and
+    // K(t+4) is loaded into registers, one chunk per group of four MFMAs;
+    // the softmax; then P V, during which K(t+4) goes to LDS and V(t+4) is
+    // loaded, one chunk per key.  So the MFMA pipe is fed throughout except
+    // for the softmax.  LDS reads and writes of one wave execute in order,
+    // so a region is rewritten only after the reads of the tile before have
+    // been served.
+    auto key_loop = [&](auto vec_c) __attribute__((always_inline)) {
+        constexpr bool VEC = decltype(vec_c)::value != 0;
+        auto load4 = [&](__amdgpu_buffer_rsrc_t r, int row, int col, int ncols)
+            __attribute__((always_inline)) {
+            if constexpr (VEC) return load4v(r, row, p.S_k, col, ncols);
+            else return load4s(r, row, p.S_k, col, ncols);
+        };
+        u32x4 rk4[T::K_PER_L], rv4[T::V_PER_L];   // one tile of K and of V in flight
+        auto load_k = [&](int t, int i) __attribute__((always_inline)) {
+            const int ci = lane + 64 * i;
+            rk4[i] = load4(rk, t * BN + ci / T::KCH, (ci % T::KCH) * 4, p.D_qk);
+        };
+        auto store_k = [&](int i) __attribute__((always_inline)) {
+            const int ci = lane + 64 * i;
             const int row = ci / T::KCH, cc = ci % T::KCH;
-            Kw[row * T::KCH + (cc ^ (row & 7))] = rg[it];
-        }
-    };
-    auto load_v = [&](int t) __attribute__((always_inline)) {
-        if (p.vec) {
-#pragma unroll
-            for (int it = 0; it < T::V_PER_L; ++it) {
-                const int ci = lane + 64 * it;
-                rg[it] = load4v(rv, t * BN + ci / T::VCH, p.S_k, (ci % T::VCH) * 4, p.D_v);
-            }
-        } else {
-#pragma unroll
-            for (int it = 0; it < T::V_PER_L; ++it) {
-                const int ci = lane + 64 * it;
-                rg[it] = load4s(rv, t * BN + ci / T::VCH, p.S_k, (ci % T::VCH) * 4, p.D_v);
-            }
-        }
-    };
-    auto store_v = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int it = 0; it < T::V_PER_L; ++it) Kw[T::K_CHUNKS + lane + 64 * it] = rg[it];
-    };
+            Kw[row * T::KCH + (cc ^ (row & 7))] = rk4[i];
+        };
+        auto load_v = [&](int t, int i) __attribute__((always_inline)) {
+            const int ci = lane + 64 * i;
+            rv4[i] = load4(rv, t * BN + ci / T::VCH, (ci % T::VCH) * 4, p.D_v);
+        };
+        auto store_v = [&](int i) __attribute__((always_inline)) {
+            Kw[T::K_CHUNKS + lane + 64 * i] = rv4[i];
+        };
 
-    // LDS reads and writes of one wave execute in order, so a region is
-    // rewritten only after the reads of the tile before have been served.
-    if (wave < ntiles) {
-        load_k(wave);
-        store_k();
-        load_v(wave);
-    }
-    for (int t = wave; t < ntiles; t += 4) {
-        const int kbase = t * BN;
-
-        // ---- S^T: lane (l32, hh) gets keys (r/4)*8 + 4hh + r%4 of query qi
-        // Operand reads run ahead of the MFMAs that use them (three K chunks,
-        // two V keys); scheduling barriers keep the compiler from sinking
-        // them back next to their use.
-        f32x16 s = f32x16{};
-        {
-            constexpr int NU = DQ / 8;
-            f32x4 ka[4];
-            auto kread = [&](int u) __attribute__((always_inline)) {
-                return __builtin_bit_cast(f32x4, Kw[l32 * T::KCH + ((2 * u + hh) ^ (l32 & 7))]);
-            };
+        if (wave < ntiles) {
 #pragma unroll
-            for (int u = 0; u < 3; ++u) ka[u] = kread(u);
+            for (int i = 0; i < T::K_PER_L; ++i) load_k(wave, i);
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                if (u + 3 < NU) ka[(u + 3) & 3] = kread(u + 3);
-                __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < T::K_PER_L; ++i) store_k(i);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s = mma32(ka[u & 3][j], qf[4 * u + j], s);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int i = 0; i < T::V_PER_L; ++i) load_v(wave, i);
         }
-        store_v();                               // V(t): the P V of tile t-4 is done
-        if (t + 4 < ntiles) load_k(t + 4);
+        for (int t = wave; t < ntiles; t += 4) {
+            const int kbase = t * BN;
+            // The loads and stores for tile t+4 run unconditionally: past
+            // the last tile of the wave they move rows that are never read
+            // (or zeros, past S_k), and keep the loop free of branches.
 
-        const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > q0);
-        if (need_mask) {
+            // ---- S^T: lane (l32, hh) gets keys (r/4)*8 + 4hh + r%4 of query
+            // qi.  K chunks are read three groups ahead of their MFMAs;
+            // scheduling barriers keep the compiler from sinking the reads
+            // (and the chunk moves) back next to their use.
+            f32x16 s = f32x16{};
+            {
+                constexpr int NU = DQ / 8;
+                f32x4 ka[4];
+                auto kread = [&](int u) __attribute__((always_inline)) {
+                    return __builtin_bit_cast(f32x4,
+                                              Kw[l32 * T::KCH + ((2 * u + hh) ^ (l32 & 7))]);
+                };
+#pragma unroll
+                for (int u = 0; u < 3; ++u) ka[u] = kread(u);
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    if (u + 3 < NU) ka[(u + 3) & 3] = kread(u + 3);
+#pragma unroll
+                    for (int i = u; i < T::V_PER_L; i += NU) store_v(i);   // V(t)
+#pragma unroll
+                    for (int i = u; i < T::K_PER_L; i += NU) load_k(t + 4, i);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) s = mma32(ka[u & 3][j], qf[4 * u + j], s);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+
+            const bool need_mask = (kbase + BN > p.S_k) || (CAUSAL && kbase + BN - 1 > q0);
+            if (need_mask) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kbase + (r >> 2) * 8 + hh * 4 + (r & 3);
+                    bool ok = key < p.S_k;
+                    if (CAUSAL) ok = ok && key <= qi;
+                    s[r] = ok ? s[r] : neg_inf();
+                }
+            }
+
+            // Every tile a wave visits holds a key visible to each of its
+            // rows (key kbase <= the first row when causal, kbase < S_k), so
+            // m is finite from the first tile on.  The running max only moves
+            // when some row's max grows by more than 2^kTau in the exponent
+            // (always on the first tile), so O and l are rescaled rarely and
+            // P stays below 2^kTau.
+            float mx = s[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+            mx = fmaxf(mx, other_half(mx));
+            if (__builtin_amdgcn_ballot_w64((mx - m) * c > kTau) != 0) {
+                const float m_new = fmaxf(m, mx);
+                const float alpha = fast_exp2((m - m_new) * c);
+                m = m_new;
+                l *= alpha;
+#pragma unroll
+                for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
+            }
+            const float mc = m * c;
+
+            float pv[16];
+            float rs = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = kbase + (r >> 2) * 8 + hh * 4 + (r & 3);
-                bool ok = key < p.S_k;
-                if (CAUSAL) ok = ok && key <= qi;
-                s[r] = ok ? s[r] : neg_inf();
+                pv[r] = fast_exp2(__builtin_fmaf(s[r], c, -mc));
+                rs += pv[r];
+            }
+            l += rs;
+
+            // ---- O^T += V^T P^T; step r uses key (r/4)*8 + 4hh + r%4; V is
+            // read two keys ahead
+            {
+                float va[3][DV / 32];
+                auto vread = [&](int r, float (&dst)[DV / 32]) __attribute__((always_inline)) {
+                    const int key = (r >> 2) * 8 + hh * 4 + (r & 3);
+#pragma unroll
+                    for (int d = 0; d < DV / 32; ++d) dst[d] = Vw[key * DV + d * 32 + l32];
+                };
+                vread(0, va[0]);
+                vread(1, va[1]);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    if (r + 2 < 16) vread(r + 2, va[(r + 2) % 3]);
+#pragma unroll
+                    for (int i = r; i < T::K_PER_L; i += 16) store_k(i);       // K(t+4)
+#pragma unroll
+                    for (int i = r; i < T::V_PER_L; i += 16) load_v(t + 4, i);  // V(t+4)
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int d = 0; d < DV / 32; ++d) o[d] = mma32(va[r % 3][d], pv[r], o[d]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
-
-        // Every tile a wave visits holds a key visible to each of its rows
-        // (key kbase <= the first row when causal, kbase < S_k), so m is
-        // finite from the first tile on.  The running max only moves when
-        // some row's max grows by more than 2^kTau in the exponent (always on
-        // the first tile), so O and l are rescaled rarely and P stays
-        // below 2^kTau.
-        float mx = s[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-        mx = fmaxf(mx, other_half(mx));
-        if (__builtin_amdgcn_ballot_w64((mx - m) * c > kTau) != 0) {
-            const float m_new = fmaxf(m, mx);
-            const float alpha = fast_exp2((m - m_new) * c);
-            m = m_new;
-            l *= alpha;
-#pragma unroll
-            for (int d = 0; d < DV / 32; ++d) o[d] *= alpha;
-        }
-        const float mc = m * c;
-
-        float pv[16];
-        float rs = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            pv[r] = fast_exp2(__builtin_fmaf(s[r], c, -mc));
-            rs += pv[r];
-        }
-        l += rs;
-
-        // ---- O^T += V^T P^T; step r uses key (r/4)*8 + 4hh + r%4
-        {
-            float va[3][DV / 32];
-            auto vread = [&](int r, float (&dst)[DV / 32]) __attribute__((always_inline)) {
-                const int key = (r >> 2) * 8 + hh * 4 + (r & 3);
-#pragma unroll
-                for (int d = 0; d < DV / 32; ++d) dst[d] = Vw[key * DV + d * 32 + l32];
-            };
-            vread(0, va[0]);
-            vread(1, va[1]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                if (r + 2 < 16) vread(r + 2, va[(r + 2) % 3]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int d = 0; d < DV / 32; ++d) o[d] = mma32(va[r % 3][d], pv[r], o[d]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-
-        if (t + 4 < ntiles) {
-            store_k();                           // K(t+4): the scores of t are done
-            load_v(t + 4);
-        }
-    }
+    };
+    if (p.vec) key_loop(IC<1>{});
+    else key_loop(IC<0>{});
 
     // ---- combination of the four waves' partial results
     __syncthreads();   // every wave is done with its K / V region
