@@ -165,9 +165,11 @@ def test_plan_for_workloads(lib, name):
         assert 3 * plan.lds_bytes <= 160 * 1024
     else:
         # LDS-direct kernel, wide heads: 8 waves x 32 rows, 64-key tiles, K
-        # ring of 4 slots and V ring of 2 slots
+        # ring of 4 slots and V ring of 2 slots (4 with the causal mask,
+        # which synchronises every second tile)
         assert (plan.block_m, plan.threads, plan.waves, plan.block_n) == (256, 512, 8, 64)
-        assert plan.lds_bytes == (4 * plan.dqk_block + 2 * plan.dv_block) * 64 * 2
+        vslots = 4 if w.causal else 2
+        assert plan.lds_bytes == (4 * plan.dqk_block + vslots * plan.dv_block) * 64 * 2
         assert plan.lds_bytes <= 160 * 1024
     bm = plan.block_m
     assert plan.dqk_block >= w.D_qk and plan.dv_block >= w.D_v

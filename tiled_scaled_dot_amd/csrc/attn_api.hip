@@ -56,7 +56,8 @@ int check_shape(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, in
 void fill_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
                int causal, int dtype, bool vector_io, tsd_plan *pl)
 {
-    const tsd::TileConfig cfg = tsd::tile_config(dtype, D_qk, D_v, vector_io, B * H, S_q);
+    const tsd::TileConfig cfg =
+        tsd::tile_config(dtype, D_qk, D_v, vector_io, B * H, S_q, causal != 0);
     std::memset(pl, 0, sizeof(*pl));
     pl->dtype = dtype;
     pl->causal = causal ? 1 : 0;

@@ -683,7 +683,8 @@ attn_fwd_32(KernelArgs p)
 //     (buffer_load_dwordx4 ... lds): no VGPR staging, no LDS write
 //     instructions.  The buffer range is the slice, so key rows >= S_k read
 //     as zero; head-dim chunks >= D read as zero through an out-of-range
-//     offset.  K and V sit in LDS rings (4 and 2 tiles for 128-wide heads):
+//     offset.  K and V sit in LDS rings (4 and 2 tiles for 128-wide heads,
+//     4 and 4 with the causal mask, which synchronises every second tile):
 //     a tile's K is read one iteration before its V, so K is fetched up to
 //     KS-1 tiles ahead and V VS-1 tiles ahead.
 //   * Each wave instruction fills 1 KB of LDS contiguously (lane i -> bytes
@@ -770,6 +771,9 @@ __host__ __device__ __attribute__((always_inline)) inline void static_for(F &&f)
 #ifndef TSD_DMA_LEAD
 #define TSD_DMA_LEAD 1
 #endif
+#ifndef TSD_BAR2
+#define TSD_BAR2 1
+#endif
 #ifndef TSD_SCHED_VALU8
 #define TSD_SCHED_VALU8 4   // VALU slots per fp8 score MFMA, in units of TSD_SCHED_VALU
 #endif
@@ -804,7 +808,7 @@ __device__ __attribute__((always_inline)) inline void schedule_iteration()
     }
 }
 
-template <int DQ, int DV, int QKB = 2>
+template <int DQ, int DV, int QKB = 2, bool BAR2 = false>
 struct Fast16 {
     static constexpr FastShape SH = fast_shape(DQ, DV);
     static constexpr int NW = SH.waves, THREADS = 64 * SH.waves, BM = 32 * SH.waves;
@@ -815,8 +819,9 @@ struct Fast16 {
     static constexpr int KT = BN * KROW, VT = BN * VROW;
     // Ring buffers of KS K tiles and VS V tiles.  Iteration t reads K(t+1)
     // (scores of the next tile) and V(t); after its barrier it refills the
-    // slots of K(t) and V(t-1) with K(t+KS) and V(t+VS-1).
-    static constexpr int KS = SH.kslots, VS = SH.vslots, U = SH.kslots;
+    // slots of K(t) and V(t-1) with K(t+KS) and V(t+VS-1).  BAR2 (a barrier
+    // every second iteration) keeps four V tiles.
+    static constexpr int KS = SH.kslots, VS = BAR2 ? 4 : SH.vslots, U = SH.kslots;
     static constexpr int K_SLOT0 = 0, V_SLOT0 = KS * KT;
     static constexpr int LDS_BYTES = KS * KT + VS * VT;
     // Waves that issue the tile loads: with two waves per SIMD (waves w and
@@ -928,7 +933,10 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(Fast16<DQ, DV>::THREA
                                                    Fast16<DQ, DV>::SH.occ)))
 attn_fwd_fast16(KernelArgs p)
 {
-    using T = Fast16<DQ, DV, QK8 ? 1 : 2>;
+    // Plain causal attention with the 8-wave shape synchronises every second
+    // key tile (measured 1-3% faster there, 1% slower without the causal mask).
+    constexpr bool BAR2 = TSD_BAR2 && CAUSAL && !EXT && !SCALED && fast_shape(DQ, DV).kslots == 4;
+    using T = Fast16<DQ, DV, QK8 ? 1 : 2, BAR2>;
     constexpr int BN = T::BN;
     constexpr int QKB = QK8 ? 1 : 2;          // bytes per Q/K element
     constexpr int KREADS = T::KCH / 2;        // 16-byte K reads per lane per 32-key block
@@ -1059,6 +1067,15 @@ attn_fwd_fast16(KernelArgs p)
         }
     }
 
+    static_assert(!BAR2 || (T::KS == 4 && T::VS == 4), "BAR2 needs four-tile rings");
+    if constexpr (BAR2) {
+        // K(0..2) and V(0..1): the tiles of iterations 0 and 1
+        issue_k(0, IC<0>{});
+        if (1 < ntiles) issue_k(1, IC<1>{});
+        if (2 < ntiles) issue_k(2, IC<2>{});
+        issue_v(0, IC<0>{});
+        if (1 < ntiles) issue_v(1, IC<1>{});
+    } else {
     // Prologue: K(0 .. KS-1) and V(0 .. VS-2) in the order the main loop
     // would have issued them (K(j) before V(j-1)), K(0) first.
     issue_k(0, IC<0>{});
@@ -1068,6 +1085,7 @@ attn_fwd_fast16(KernelArgs p)
         if constexpr (j - 1 < T::VS - 1)
             if (j - 1 < ntiles) issue_v(j - 1, IC<j - 1>{});
     });
+    }
 
     // ---- per-row scale (SCALED): this lane's query block's Q scale, folded
     // into the exponent factor; a negative scale flips Q's sign, a zero one
@@ -1221,8 +1239,13 @@ attn_fwd_fast16(KernelArgs p)
 
     // ---- prologue: scores of tile 0.  K(0) was the first load issued; every
     // other prologue load may still be in flight when all of them exist.
+    if constexpr (BAR2) {
+        if (ntiles > 2) wait_loads<2 * T::K_PER_W + 2 * T::V_PER_W>();
+        else wait_loads<0>();
+    } else {
     if (ntiles >= T::KS) wait_loads<(T::KS - 1) * T::K_PER_W + (T::VS - 1) * T::V_PER_W>();
     else wait_loads<0>();
+    }
     __syncthreads();
     f32x16 sc[2][2];     // scores of tiles t and t+1, alternating by parity
     float mxs[2];        // their row maxima (both lane halves)
@@ -1314,11 +1337,29 @@ attn_fwd_fast16(KernelArgs p)
         // iterations t-VS+2 .. t-1, all full while t+KS-1 < ntiles; near the
         // end wait for everything.  After the barrier every wave is done with
         // the slots of K(t) and V(t-1), which this iteration refills.
+        if constexpr (BAR2) {
+            // A barrier every second iteration: the leading wave of a SIMD
+            // pair runs on into the next tile while the other finishes.  At
+            // an even iteration t everything issued two iterations ago (the
+            // tiles of t and t+1) must be resident; then the slots of
+            // K(t-1), K(t), V(t-2) and V(t-1), which no wave reads from here
+            // to the next barrier, are refilled with the tiles of t+2 and
+            // t+3.
+            if constexpr (u % 2 == 0) {
+                wait_loads<0>();
+                __syncthreads();
+                if (t + 3 < ntiles) issue_k(t + 3, IC<(u + 3) % 4>{});
+                if (t + 4 < ntiles) issue_k(t + 4, IC<u>{});
+                if (t + 2 < ntiles) issue_v(t + 2, IC<(u + 2) % 4>{});
+                if (t + 3 < ntiles) issue_v(t + 3, IC<(u + 3) % 4>{});
+            }
+        } else {
         if (t + T::KS - 1 < ntiles) wait_loads<(T::VS - 2) * T::LOADS>();
         else wait_loads<0>();
         __syncthreads();
         if (t + T::KS < ntiles) issue_k(t + T::KS, IC<u % T::KS>{});
         if (t + T::VS - 1 < ntiles) issue_v(t + T::VS - 1, IC<(u + T::VS - 1) % T::VS>{});
+        }
         if (!active) {
             // With a window a wave can be idle on tile t and busy on t+1:
             // then it still forms the scores of t+1 here.
@@ -1924,7 +1965,7 @@ hipError_t dispatch_causal(int dtype, bool causal, int64_t grid, const KernelArg
 #define TSD_SPLIT_BELOW 512
 #endif
 TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec, int64_t slices,
-                       int64_t S_q)
+                       int64_t S_q, bool causal)
 {
     TileConfig t;
     t.dqk_block = pad_dim(D_qk);
@@ -1941,7 +1982,8 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec, int64_t s
         t.waves = sh.waves;
         t.threads = 64 * sh.waves;
         t.block_n = 64;
-        t.lds_bytes = (sh.kslots * t.dqk_block + sh.vslots * t.dv_block) * 64 * 2;
+        const int vslots = (TSD_BAR2 && causal && sh.kslots == 4) ? 4 : sh.vslots;
+        t.lds_bytes = (sh.kslots * t.dqk_block + vslots * t.dv_block) * 64 * 2;
     } else if (t.split_keys) {
         // widths padded to 64, 96 or 128 (MFMA work grows with the padding)
         t.dqk_block = pad_split(D_qk);
