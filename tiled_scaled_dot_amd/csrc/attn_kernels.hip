@@ -933,9 +933,10 @@ __global__ void __attribute__((amdgpu_flat_work_group_size(Fast16<DQ, DV>::THREA
                                                    Fast16<DQ, DV>::SH.occ)))
 attn_fwd_fast16(KernelArgs p)
 {
-    // Plain causal attention with the 8-wave shape synchronises every second
-    // key tile (measured 1-3% faster there, 1% slower without the causal mask).
-    constexpr bool BAR2 = TSD_BAR2 && CAUSAL && !EXT && !SCALED && fast_shape(DQ, DV).kslots == 4;
+    // Causal attention with the 8-wave shape synchronises every second key
+    // tile (measured 1-3% faster there, 1% slower without the causal mask;
+    // the per-block scaled kernels would spill).
+    constexpr bool BAR2 = TSD_BAR2 && CAUSAL && !SCALED && fast_shape(DQ, DV).kslots == 4;
     using T = Fast16<DQ, DV, QK8 ? 1 : 2, BAR2>;
     constexpr int BN = T::BN;
     constexpr int QKB = QK8 ? 1 : 2;          // bytes per Q/K element

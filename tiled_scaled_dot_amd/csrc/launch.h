@@ -126,8 +126,8 @@ struct TileConfig {
 };
 
 // `slices` and `S_q` size the grid (0: not known, no key split).
-// `causal` only changes the reported LDS size (plain causal launches keep
-// four V tiles).
+// `causal` only changes the reported LDS size (causal launches of the
+// 8-wave shape keep four V tiles).
 TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec, int64_t slices = 0,
                        int64_t S_q = 0, bool causal = false);
 
