@@ -1341,18 +1341,21 @@ attn_fwd_fast16(KernelArgs p)
         if constexpr (BAR2) {
             // A barrier every second iteration: the leading wave of a SIMD
             // pair runs on into the next tile while the other finishes.  At
-            // an even iteration t everything issued two iterations ago (the
-            // tiles of t and t+1) must be resident; then the slots of
-            // K(t-1), K(t), V(t-2) and V(t-1), which no wave reads from here
-            // to the next barrier, are refilled with the tiles of t+2 and
-            // t+3.
+            // an even iteration t everything issued before (what iterations
+            // t and t+1 read) must be resident; then the slots of K(t-1),
+            // K(t), V(t-2) and V(t-1), which no wave reads from here to the
+            // next barrier, take what iterations t+2 and t+3 read: K(t+3)
+            // and V(t+2) right after the barrier, K(t+4) and V(t+3) one
+            // iteration later, which halves the leading waves' load burst
+            // after a barrier.
             if constexpr (u % 2 == 0) {
                 wait_loads<0>();
                 __syncthreads();
                 if (t + 3 < ntiles) issue_k(t + 3, IC<(u + 3) % 4>{});
-                if (t + 4 < ntiles) issue_k(t + 4, IC<u>{});
                 if (t + 2 < ntiles) issue_v(t + 2, IC<(u + 2) % 4>{});
-                if (t + 3 < ntiles) issue_v(t + 3, IC<(u + 3) % 4>{});
+            } else {
+                if (t + 3 < ntiles) issue_k(t + 3, IC<(u + 3) % 4>{});
+                if (t + 2 < ntiles) issue_v(t + 2, IC<(u + 2) % 4>{});
             }
         } else {
         if (t + T::KS - 1 < ntiles) wait_loads<(T::VS - 2) * T::LOADS>();
