@@ -120,6 +120,34 @@ def test_edge_shapes(case, causal, dtype):
     check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"{case} c={causal} {dtype}")
 
 
+# ------------------------------------ causal key-tile counts, 8-wave shape
+@pytest.mark.parametrize("n_tiles", list(range(1, 10)))
+def test_causal_tile_counts(n_tiles):
+    """Causal bf16 attention at D = 128 over 1-9 key tiles of 64 (ragged by
+    13 keys): the causal launches of the 8-wave shape synchronise every
+    second tile and split each pair's loads over two tiles, so odd and even
+    tile counts, and counts below the ring depth, take different ends of
+    the loop."""
+    S = 64 * n_tiles - 13
+    print(f"[case] causal tiles={n_tiles} S={S}", flush=True)
+    q, k, v = random_inputs((1, 2, S + 200, 128), (1, 2, S, 128), (1, 2, S, 128), "bf16",
+                            seed=6000 + n_tiles)
+    o, lse = run_gpu(q, k, v, 1 / math.sqrt(128), True)
+    o_ref, lse_ref = run_oracle(q, k, v, 1 / math.sqrt(128), True)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, "bf16", f"causal tiles={n_tiles}")
+    # the extended kernel, causal at the bottom right (query i sees keys
+    # j <= i + S_k - S_q), S_q = S_k - 40
+    qe = q[:, :, : max(S - 40, 1)].contiguous()
+    off = S - qe.shape[2]
+    o, lse = tsd.attn_fwd_ext(qe.to(DEV), k.to(DEV), v.to(DEV), scale=1 / math.sqrt(128),
+                              causal=True, causal_offset=off)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_ref_ext(qe.double().numpy(), k.double().numpy(),
+                                         v.double().numpy(), 1 / math.sqrt(128), True,
+                                         causal_offset=off)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, "bf16", f"ext causal tiles={n_tiles}")
+
+
 # ------------------------------------------------------ the two f32 kernels
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [
