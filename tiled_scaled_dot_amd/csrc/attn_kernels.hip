@@ -782,16 +782,17 @@ __device__ __attribute__((always_inline)) inline void sched_group()
 {
     if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
 }
-// NS score MFMAs (RS K reads and VS x TSD_SCHED_VALU VALU slots each: an
-// fp8 score MFMA takes twice the cycles of a 16-bit one and reads two
-// chunks; four times the VALU slots measured 3-4% faster than twice), then
-// NP P V MFMAs (two transposed V reads each).
-template <int NS, int NP, int RS = 1, int VS = 1>
+// NS score MFMAs (RS K reads and VS x VA VALU slots each: an fp8 score
+// MFMA takes twice the cycles of a 16-bit one and reads two chunks; four
+// times the VALU slots measured 3-4% faster than twice), then NP P V MFMAs
+// (two transposed V reads and VA VALU slots each).  VA is 3 for 128-wide
+// Q/K and 4 for 64-wide Q/K, whose tiles have half the score MFMAs for the
+// same softmax work.
+template <int NS, int NP, int RS = 1, int VS = 1, int VA = TSD_SCHED_VALU>
 __device__ __attribute__((always_inline)) inline void schedule_iteration()
 {
     if constexpr (TSD_SCHED) {
         constexpr int LEAD = TSD_SCHED_LEAD < NS * RS ? TSD_SCHED_LEAD : NS * RS;
-        constexpr int VA = TSD_SCHED_VALU;
         sched_group<0x100, LEAD>();
         sched_group<0x002, 2 * VA>();
         static_for<0, NS>([&](auto ic) __attribute__((always_inline)) {
@@ -1402,7 +1403,8 @@ attn_fwd_fast16(KernelArgs p)
         if constexpr (QK8)
             schedule_iteration<2 * (DQ / 64), 4 * (DV / 32), 2, TSD_SCHED_VALU8>();
         else
-            schedule_iteration<2 * (DQ / 16), 4 * (DV / 32)>();
+            schedule_iteration<2 * (DQ / 16), 4 * (DV / 32), 1, 1,
+                               DQ <= 64 ? TSD_SCHED_VALU + 1 : TSD_SCHED_VALU>();
     };
 
     for (int t0 = 0; t0 < ntiles; t0 += T::U) {
