@@ -29,8 +29,10 @@
 //     puts one query per lane column, so each lane holds 16 keys of a single
 //     query and the row max / sum are in-lane plus one swap with lane^32.
 //   * The S^T accumulator layout is exactly the B operand layout of the
-//     P V MFMA (O^T = V^T P^T), so P never leaves registers.  V is written
-//     to LDS transposed (d-major) so the A operand reads 8 contiguous keys.
+//     P V MFMA (O^T = V^T P^T), so P never leaves registers.  The A operand
+//     needs 8 consecutive keys of one V column per lane: the generic
+//     kernels write V to LDS d-major, the main kernel keeps the key-major
+//     rows its LDS-direct loads land and reads them with ds_read_b64_tr_b16.
 //   * Key rows read for the score MFMA are permuted (sigma below) so that
 //     each lane's P values cover 8 consecutive keys, which makes every LDS
 //     operand read a single 16-byte access.  Permuting keys is legal: the
