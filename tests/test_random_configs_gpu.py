@@ -1,8 +1,10 @@
 """Seeded random configurations across the entry points, each against the
-fp64 oracle (the same bars as the targeted tests).  Shapes are drawn so
-that every run stays small (a few million score elements at most) while
-covering ragged sizes, head-dim tails, D_qk != D_v, both 16-bit dtypes,
-causal offsets, windows, key ranges, grouped heads and chunk counts."""
+fp64 oracle (the same bars as the targeted tests).  Most shapes are drawn
+so that the oracle checks every output (a few million score elements at
+most) while covering ragged sizes, head-dim tails, D_qk != D_v, both 16-bit
+dtypes, causal offsets, windows, key ranges, grouped heads and chunk
+counts; a last group draws grids of up to 6000 x 6000 per slice and checks
+a row sample."""
 import math
 import random
 
@@ -119,3 +121,30 @@ def test_random_scaled(seed):
                                             ks.double().numpy(), c["q_block"], c["k_block"],
                                             c["causal"])
     check(o, lse, o_ref, lse_ref, vdt, f"scaled {c}")
+
+
+def draw_large(rng):
+    dtype = rng.choice(["f16", "bf16", "bf16", "f32"])
+    D_qk = rng.choice([64, 128, rng.randint(1, 128)])
+    return dict(dtype=dtype, B=rng.randint(1, 2), H=rng.randint(1, 6), S_q=rng.randint(1, 6000),
+                S_k=rng.randint(1, 6000), D_qk=D_qk, D_v=rng.choice([64, 128, rng.randint(1, 128)]),
+                causal=rng.random() < 0.5,
+                scale=rng.choice([1 / math.sqrt(D_qk), rng.uniform(-0.4, 0.4)]))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_large_sampled_rows(seed):
+    """Grids of up to a few thousand rows and keys (many key tiles, several
+    workgroups per CU), every output computed on the GPU and a random sample
+    of rows, plus the first and last, checked exactly against the oracle."""
+    rng = random.Random(4000 + seed)
+    c = draw_large(rng)
+    print(f"[case] large {c}", flush=True)
+    q, k, v = random_inputs((c["B"], c["H"], c["S_q"], c["D_qk"]), (c["B"], c["H"], c["S_k"], c["D_qk"]),
+                            (c["B"], c["H"], c["S_k"], c["D_v"]), c["dtype"], seed=4000 + seed)
+    o, lse = tsd.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=c["scale"], causal=c["causal"])
+    torch.cuda.synchronize()
+    rows = sorted({0, c["S_q"] - 1} | {rng.randrange(c["S_q"]) for _ in range(48)})
+    o_ref, lse_ref = oracle.attn_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                     c["scale"], c["causal"], rows=rows)
+    check(o[:, :, rows], lse[:, :, rows], o_ref, lse_ref, c["dtype"], f"large {c}")
