@@ -365,3 +365,34 @@ def test_splitkv_workspace_checks(lib):
     assert tsd.attn_fwd_splitkv_raw(*args, 0x60000000 + 64, ws) == 3  # not 256-aligned
     assert tsd.attn_fwd_splitkv_raw(*args, OA, ws) == 5             # workspace on O
     assert tsd.attn_fwd_splitkv_raw(*args, KA - 256, ws) == 5       # workspace into K
+
+
+def test_planner_and_checks_from_many_threads(lib):
+    """The library keeps no state: plans computed by eight host threads at
+    once (ctypes drops the GIL for the call) equal the single-threaded ones,
+    and invalid calls return their status from every thread."""
+    import random
+    from concurrent.futures import ThreadPoolExecutor
+    rng = random.Random(7)
+    cases = [(rng.randint(1, 4), rng.randint(1, 40), rng.randint(1, 20000), rng.randint(1, 20000),
+              rng.randint(1, 128), rng.randint(1, 128), rng.random() < 0.5,
+              rng.choice(["f32", "f16", "bf16"])) for _ in range(64)]
+    fields = [f for f, _ in tsd.TsdPlan._fields_]
+
+    def as_tuple(plan):
+        return tuple(getattr(plan, f) for f in fields)
+
+    want = [as_tuple(tsd.attn_fwd_plan(*c)) for c in cases]
+
+    def worker(seed):
+        r = random.Random(seed)
+        for _ in range(300):
+            i = r.randrange(len(cases))
+            assert as_tuple(tsd.attn_fwd_plan(*cases[i])) == want[i]
+            # a null Q: rejected on the host before any HIP call
+            assert tsd.attn_fwd_raw(0, 16, 16, 16, 0, 1, 1, 8, 8, 64, 64, 0.1, False,
+                                    "bf16") == 1   # TSD_ERR_NULL
+        return True
+
+    with ThreadPoolExecutor(8) as ex:
+        assert all(ex.map(worker, range(8)))
