@@ -8,7 +8,8 @@ max absolute error over every active output element:
        LSE only sees f32 score/sum rounding, so it is far tighter than O).
 Full-size workloads compare a row sample (every 16th row, rows 0, 1, S_q-1,
 and both sides of every 128-row block boundary); rows are independent, so
-each sampled row is an exact check.
+each sampled row is an exact check.  The 16-bit workloads of up to 2^31
+query-key pairs are also checked on every row.
 """
 import math
 
@@ -79,6 +80,22 @@ def test_workload_sampled_rows(name):
     del o, lse
     o_ref, lse_ref = run_oracle(q, k, v, w.scale, w.causal, rows=rows)
     check(o_s, lse_s, o_ref, lse_ref, w.dtype, f"{name} ({len(rows)} rows/slice)")
+
+
+FULL_16BIT = [n for n in LARGE if WORKLOADS[n].B * WORKLOADS[n].H * WORKLOADS[n].S_q
+              * WORKLOADS[n].S_k <= 2 ** 31]
+
+
+@pytest.mark.parametrize("name", FULL_16BIT)
+def test_workload_every_row(name):
+    """The 16-bit workloads whose oracle finishes in seconds (up to 2^31
+    query-key pairs), every output row checked."""
+    w = WORKLOADS[name]
+    print(f"[case] {name} (every row)", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = run_gpu(q, k, v, w.scale, w.causal)
+    o_ref, lse_ref = run_oracle(q, k, v, w.scale, w.causal)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, w.dtype, f"{name} (every row)")
 
 
 # ------------------------------------------------------------- edge cases
