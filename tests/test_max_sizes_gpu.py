@@ -51,15 +51,59 @@ def check_rows(o, lse, q, k, v, rows, scale, causal, what):
     assert err_o <= TOL_O and err_l <= TOL_LSE, what
 
 
-def test_longest_key_slice():
-    """K and V slices of 2^31 - 256 bytes (8388607 keys), 300 query rows."""
-    S_q, S_k = 300, MAX_ROWS
-    print(f"[case] bf16 S_q={S_q} S_k={S_k} D={D} non-causal", flush=True)
-    q, k, v = random_inputs((1, 1, S_q, D), (1, 1, S_k, D), (1, 1, S_k, D), "bf16", seed=31)
+@pytest.fixture(scope="module")
+def long_kv():
+    """K and V slices of 2^31 - 256 bytes (8388607 keys): CPU bf16, GPU,
+    and float64 for the oracle; with 300 query rows."""
+    q, k, v = random_inputs((1, 1, 300, D), (1, 1, MAX_ROWS, D), (1, 1, MAX_ROWS, D), "bf16",
+                            seed=31)
+    return dict(q=q, k=k, v=v, kg=k.cuda(), vg=v.cuda(), kd=k.double().numpy(),
+                vd=v.double().numpy())
+
+
+def test_longest_key_slice(long_kv):
+    q, k, v = long_kv["q"], long_kv["k"], long_kv["v"]
+    print(f"[case] bf16 S_q={q.shape[2]} S_k={k.shape[2]} D={D} non-causal", flush=True)
     scale = 1 / np.sqrt(D)
-    o, lse = tsd.attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=False)
+    o, lse = tsd.attn_fwd(q.cuda(), long_kv["kg"], long_kv["vg"], scale=scale, causal=False)
     torch.cuda.synchronize()
     check_rows(o, lse, q, k, v, [0, 1, 255, 256, 298, 299], scale, False, "longest key slice")
+
+
+def check_ext_rows(o, lse, long_kv, rows, scale, what, **mask):
+    o_s, lse_s = to_np(o[:, :, rows]), to_np(lse[:, :, rows])
+    o_ref, lse_ref = oracle.attn_ref_ext(long_kv["q"].double().numpy(), long_kv["kd"],
+                                         long_kv["vd"], scale, rows=rows, **mask)
+    err_o = float(np.max(np.abs(o_s - o_ref)))
+    err_l = float(np.max(np.abs(lse_s - lse_ref)))
+    print(f"[parity] {what}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+    assert np.isfinite(o_s).all() and np.isfinite(lse_s).all()
+    assert err_o <= TOL_O and err_l <= TOL_LSE, what
+
+
+def test_longest_key_slice_window_at_the_end(long_kv):
+    """Bottom-right causal with a 3000-key window: every row's keys lie in
+    the last 3300 of the slice, so the key tiles start near byte 2^31."""
+    q = long_kv["q"]
+    S_q, S_k = q.shape[2], MAX_ROWS
+    mask = dict(causal=True, causal_offset=S_k - S_q, window=3000)
+    print(f"[case] ext bf16 S_q={S_q} S_k={S_k} {mask}", flush=True)
+    scale = 1 / np.sqrt(D)
+    o, lse = tsd.attn_fwd_ext(q.cuda(), long_kv["kg"], long_kv["vg"], scale=scale, **mask)
+    torch.cuda.synchronize()
+    check_ext_rows(o, lse, long_kv, [0, 1, 150, 298, 299], scale, "window at the end", **mask)
+
+
+def test_longest_key_slice_splitkv(long_kv):
+    """Split-KV over the whole slice: 16 chunks merged."""
+    q = long_kv["q"][:, :, :64].contiguous()
+    print(f"[case] split-KV bf16 S_q=64 S_k={MAX_ROWS} 16 chunks", flush=True)
+    scale = 1 / np.sqrt(D)
+    o, lse = tsd.attn_fwd_splitkv(q.cuda(), long_kv["kg"], long_kv["vg"], scale=scale,
+                                  n_splits=16)
+    torch.cuda.synchronize()
+    check_ext_rows(o, lse, dict(long_kv, q=q), [0, 31, 63], scale, "split-KV 16 chunks",
+                   causal=False)
 
 
 @pytest.mark.parametrize("causal", [False, True])
