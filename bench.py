@@ -14,6 +14,12 @@ kernel runs on (torch's current stream, which is the stream the binding
 passes to the library).  `cpu_baseline` times the fp64 CPU oracle on a
 bounded row sample of the same workload.
 
+Before the warm-up steps the step runs back to back for --settle-s seconds
+(default 1): an idle MI355X starts at a low engine clock and needs tens of
+launches of the headline size to reach the clock it holds under this load,
+so a handful of warm-up steps alone leaves the ramp inside the timed steps.
+The timed region is exactly --steps steps either way.
+
 --workload also selects the extended entry points' workloads (key offset,
 sliding window, split-KV with its merge, grouped K/V heads); their FLOPs
 count 2*(D_qk+D_v) per visible (query, key) pair, and a split-KV step is
@@ -51,9 +57,9 @@ def parse():
     ap.add_argument("--cpu-row-stride", type=int, default=2,
                     help="oracle sample: every N-th query row of every head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-sclk", action="store_true",
-                    help="skip the shader-clock reading (rocm-smi child process); for runs "
-                         "under a profiler whose preload initialises the GPU in every child")
+    ap.add_argument("--settle-s", type=float, default=1.0,
+                    help="before the warm-up steps, run the step back to back for this long "
+                         "so that the engine clock has left its idle state")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps launches of a plain device "
                          "copy of this many MiB (counter calibration for HBM traffic)")
@@ -64,6 +70,12 @@ def parse():
                          "WRITE_SIZE of this benchmark, then of --copy-probe-mib)")
     ap.add_argument("--copy-mib", type=int, default=1024,
                     help="size the --copy-probe-mib run used (for --record-traffic)")
+    ap.add_argument("--counter-summary", metavar="FOLDER",
+                    help="instead of the benchmark, summarise a rocprofv3 --pmc folder: per "
+                         "kernel, the shader clock from GRBM_COUNT, the MFMA pipe's busy "
+                         "fraction and the rate against the peak at that clock")
+    ap.add_argument("--skip-dispatches", type=int, default=0,
+                    help="--counter-summary: leave out the first N dispatches (clock ramp)")
     return ap.parse_args()
 
 
@@ -179,31 +191,78 @@ def record_traffic(args) -> int:
     return 0
 
 
-def measure_sclk(step, torch, limit_s: float = 15.0):
-    """Shader clock (MHz) while `step` runs back to back: rocm-smi is started
-    as a child process and the step is launched until it has answered.  The
-    rated peak assumes 2.4 GHz; under this load the clock sits lower.
-    Returns None where rocm-smi is not available."""
-    import re
-    import subprocess
+def counter_summary(folder: str, skip: int = 0) -> int:
+    """Per kernel of a rocprofv3 --pmc folder (csv output), averaged over the
+    dispatches after the first `skip`:
+      clock_mhz        GRBM_COUNT / XCDs / duration: GRBM_COUNT counts the
+                       engine clock on every XCD and rocprofv3 sums the XCDs
+      gui_active       GRBM_GUI_ACTIVE / GRBM_COUNT (busy fraction)
+      mfma_busy        SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x clock cycles)
+      sq_busy          SQ_BUSY_CYCLES / (shader arrays x clock cycles)
+      mfma_tflops      SQ_INSTS_VALU_MFMA_MOPS_<dtype> x 512 FLOP / duration
+      pct_peak_at_clock  that rate against the dense peak of the dtype at
+                       the measured clock (peak x clock / 2400 MHz)
+    Counters missing from the folder leave their fields out."""
+    import csv
+    import glob
 
-    try:
-        proc = subprocess.Popen(["rocm-smi", "--showclocks"], stdout=subprocess.PIPE,
-                                stderr=subprocess.DEVNULL, text=True)
-    except OSError:
-        return None
-    t0 = time.perf_counter()
-    while proc.poll() is None and time.perf_counter() - t0 < limit_s:
-        for _ in range(10):
-            step()
-        torch.cuda.synchronize()
-    try:
-        out = proc.communicate(timeout=max(1.0, limit_s - (time.perf_counter() - t0)))[0]
-    except subprocess.TimeoutExpired:
-        proc.kill()
-        return None
-    m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", out, flags=re.I)
-    return float(m.group(1)) if m else None
+    agent = {}
+    for path in glob.glob(os.path.join(folder, "**", "*agent_info.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Agent_Type") == "GPU":
+                    agent = row
+    xcc = int(agent.get("Num_Xcc", 8))
+    simds = int(agent.get("Simd_Count", 1024))
+    arrays = int(agent.get("Array_Count", 32))
+    disp = {}
+    for path in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                d = disp.setdefault(int(row["Dispatch_Id"]), {
+                    "kernel": row["Kernel_Name"],
+                    "ns": int(row["End_Timestamp"]) - int(row["Start_Timestamp"])})
+                d[row["Counter_Name"]] = float(row["Counter_Value"])
+    if not disp:
+        raise SystemExit(f"no counter rows in {folder}")
+    out = {}
+    for did in sorted(disp)[skip:]:
+        d = disp[did]
+        out.setdefault(d["kernel"], []).append(d)
+    mops_peak = {"BF16": PEAK_TFLOPS["bf16"], "F16": PEAK_TFLOPS["f16"],
+                 "F8": PEAK_TFLOPS["fp8_e4m3"], "F32": PEAK_TFLOPS["f32"]}
+    result = {}
+    for kernel, ds in out.items():
+        ns = sum(d["ns"] for d in ds) / len(ds)
+        r = {"dispatches": len(ds), "mean_ns": round(ns)}
+
+        def mean(counter):
+            vals = [d[counter] for d in ds if counter in d]
+            return sum(vals) / len(vals) if vals else None
+
+        cnt = mean("GRBM_COUNT")
+        if cnt:
+            mhz = cnt / xcc / ns * 1e3
+            cycles = cnt / xcc
+            r["clock_mhz"] = round(mhz, 1)
+            if mean("GRBM_GUI_ACTIVE") is not None:
+                r["gui_active"] = round(mean("GRBM_GUI_ACTIVE") / cnt, 4)
+            if mean("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+                r["mfma_busy"] = round(mean("SQ_VALU_MFMA_BUSY_CYCLES") / (simds * cycles), 4)
+            if mean("SQ_BUSY_CYCLES") is not None:
+                r["sq_busy"] = round(mean("SQ_BUSY_CYCLES") / (arrays * cycles), 4)
+        for tag, peak in mops_peak.items():
+            mops = mean(f"SQ_INSTS_VALU_MFMA_MOPS_{tag}")
+            if mops:
+                tf = mops * 512.0 / (ns * 1e-9) / 1e12
+                r[f"mfma_tflops_{tag.lower()}"] = round(tf, 1)
+                r[f"pct_of_{tag.lower()}_peak"] = round(100.0 * tf / peak, 2)
+                if cnt:
+                    r[f"pct_of_{tag.lower()}_peak_at_clock"] = round(
+                        100.0 * tf / (peak * r["clock_mhz"] / 2400.0), 2)
+        result[kernel] = r
+    print(json.dumps(result, indent=1))
+    return 0
 
 
 def cpu_baseline(w, q, k, v, stride: int, scales=None):
@@ -264,6 +323,8 @@ def main():
 
     if args.record_traffic:
         return record_traffic(args)
+    if args.counter_summary:
+        return counter_summary(args.counter_summary, args.skip_dispatches)
     if args.copy_probe_mib:
         return copy_probe(args.copy_probe_mib, args.steps)
 
@@ -340,6 +401,16 @@ def main():
         for ph in phases:
             ph()
 
+    # Clock settle: an idle GPU starts at a low engine clock and needs tens
+    # of launches of this size to reach the clock it holds under load.
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(4):
+            step()
+        settle_steps += 4
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_settle
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -369,7 +440,6 @@ def main():
     torch.cuda.synchronize()
     kernel_ms = a0.elapsed_time(a1) / args.steps
     extra["attn_ms_in_step"] = round(launch_ms[0], 4)
-    sclk_mhz = None if args.no_sclk else measure_sclk(step, torch)
 
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -425,13 +495,8 @@ def main():
                        f"seed {w.seed}" if w.dist == "normal" else f"{w.dist}(-1,1), seed {w.seed}"),
             "flops_per_step": flops,
             "pct_of_mfma_peak": round(100.0 * (flops / (kernel_ms * 1e-3) / 1e12) / peak, 2),
-            # the rated peak assumes 2.4 GHz; the clock read while the same
-            # step runs back to back after the timed steps gives the peak at
-            # the clock the kernel actually runs at
-            "sclk_mhz": sclk_mhz,
-            "pct_of_mfma_peak_at_sclk": (
-                round(100.0 * (flops / (kernel_ms * 1e-3) / 1e12) / (peak * sclk_mhz / 2400.0), 2)
-                if sclk_mhz else None),
+            "settle_s": round(settle_s, 2),
+            "settle_steps": settle_steps,
             "min_bytes_per_step": min_bytes,
             "attn_bytes_per_launch": attn_bytes,
             **extra,

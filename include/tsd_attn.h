@@ -110,9 +110,16 @@ TSD_API int attn_fwd(const void *Q, const void *K, const void *V, void *O, float
 
 /*
  * attn_fwd_plan — fill `out` with the plan attn_fwd would use for these
- * sizes (no HIP call, no device access).  Pointer alignment is not known
- * here, so `vector_io` reports what aligned buffers would get.  Returns the
- * same shape/dtype statuses as attn_fwd (TSD_ERR_NULL if out is NULL).
+ * sizes (no HIP call, no device access).  It is this library's form of the
+ * launch description that tiny.accy.kernel.library.attention attaches to
+ * its scaled-dot-product specialization (the `launch` / `schedule` entries:
+ * a 3-D grid of thread blocks over the value, query and batch axes, whose
+ * grid and block sizes that page's first unit test reads back): here a 1-D
+ * grid of `grid` workgroups of `threads` threads, one per (query block of
+ * `block_m` rows, slice), the slices being that page's batch axis (b, h).
+ * Pointer alignment is not known here, so `vector_io` reports what aligned
+ * buffers would get.  Returns the same shape/dtype statuses as attn_fwd
+ * (TSD_ERR_NULL if out is NULL).
  */
 TSD_API int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
                           int64_t D_qk, int64_t D_v, int causal, int dtype,
@@ -121,8 +128,13 @@ TSD_API int attn_fwd_plan(int64_t B, int64_t H, int64_t S_q, int64_t S_k,
 /*
  * attn_fwd_plan_block — for workgroup `block` (0 <= block < plan->grid),
  * report the query block, the (batch*H + head) slice and the number of key
- * tiles it visits, exactly as the kernel derives them (host only).
- * Returns TSD_ERR_SHAPE if `block` is out of range.
+ * tiles it visits, exactly as the kernel derives them (host only): the
+ * block-to-coordinates map of the schedule above (tiny.accy.kernel.library.
+ * attention, the specialization's thread-block schedule), and the key-tile
+ * count of the FA-1 kernels (VeriTile, "FlashAttention1.NaiveRefinement":
+ * numKVBlocks tiles of Bk keys cover S_k, and a causal query block stops at
+ * the tile of its last row).  Returns TSD_ERR_SHAPE if `block` is out of
+ * range, TSD_ERR_NULL if `plan` is NULL.
  */
 TSD_API int attn_fwd_plan_block(const tsd_plan *plan, int64_t S_q, int64_t S_k,
                                 int64_t block, int64_t *q_block, int64_t *slice,
@@ -230,7 +242,11 @@ TSD_API int attn_merge(const float *O_parts, const float *LSE_parts, int64_t n_p
                        void *O, float *LSE, int dtype, void *stream);
 
 /*
- * attn_splitkv_plan — the chunking attn_fwd_splitkv uses (host only).
+ * attn_splitkv_plan — the chunking attn_fwd_splitkv uses (host only): the
+ * launch description (tiny.accy.kernel.library.attention, the
+ * specialization's `launch` entry) of a pass over key chunks whose partial
+ * results a continuation merges (VeriTile proof coverage,
+ * attention_fwd_triton3 cases 3 and 4).
  * n_splits <= 0 lets the library choose: enough chunks that one round of
  * workgroups covers the 256 compute units, chunks of at least 512 keys,
  * at most 256 chunks.  Reports the chunk count actually used (chunks are
@@ -277,10 +293,10 @@ TSD_API int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *
  *       same 16-bit dtype as V.  fp8 scores run on the fp8 MFMA.
  *   V [B,H,S_k,D_v], O [B,H,S_q,D_v] of `dtype` (TSD_F16 / TSD_BF16);
  *       LSE [B,H,S_q] f32 or NULL.
- *   Q_scale [B,H,ceil(S_q/q_block)] f32, any finite values;
- *   K_scale [B,H,ceil(S_k/k_block)] f32, finite and >= 0 (a negative or NaN
- *       key scale gives unspecified results: the kernel takes the row max of
- *       the scaled scores as the scale times the raw row max).
+ *   Q_scale [B,H,ceil(S_q/q_block)] f32 and K_scale [B,H,ceil(S_k/k_block)]
+ *       f32: any finite values, of either sign, zero included (the scales
+ *       live in device memory and are not inspected on the host: NaN or
+ *       infinite scales give unspecified results).
  *   q_block >= 1; k_block a multiple of 64 (the kernel's key tile).
  * Fast path only: every buffer but the scales 16-byte aligned, D_v a
  * multiple of 8, D_qk a multiple of 8 (16 for fp8); with fp8, D_qk in
@@ -293,7 +309,11 @@ TSD_API int attn_fwd_scaled(const void *Q, const void *K, const void *V, void *O
                             int64_t D_qk, int64_t D_v, int64_t q_block, int64_t k_block,
                             int causal, int qk_dtype, int dtype, void *stream);
 
-/* attn_status_string — static text for a status code (never NULL). */
+/* attn_status_string — static text for a status code (never NULL).  The
+ * codes name the premise a call broke: the refinement theorems' 0 < S_k and
+ * D <= block width (VeriTile, "FlashAttention1.NaiveRefinement"), the
+ * disjoint output region of the coverage page's region premises (VeriTile
+ * proof coverage), a finite scale, and this library's own limits. */
 TSD_API const char *attn_status_string(int status);
 
 #ifdef __cplusplus

@@ -76,3 +76,48 @@ def test_record_and_lookup_traffic(tmp_path, monkeypatch):
     src.write_text("int v = 2; // kernel source v2\n")
     assert bench.stored_traffic("bf16_b1h32_s16384_d128_causal") is None
     assert bench.stored_traffic("no_such_workload") is None
+
+
+@pytest.mark.parametrize("S_q", [2048, 4096, 16384])
+def test_sample_rows_visit_every_row_position_of_a_wave(S_q):
+    """The full-size row samples see each of the 32 row positions of a wave
+    (a wave owns 32 consecutive query rows), and the stride-67 subsample of
+    the 16k fp8 test does too."""
+    from tiled_scaled_dot_amd.workloads import sample_rows
+
+    samples = [sample_rows(S_q)] + ([sample_rows(S_q, stride=67)] if S_q >= 67 * 32 else [])
+    for rows in samples:
+        assert {r % 32 for r in rows} == set(range(32))
+        assert {0, 1, S_q - 1} <= set(rows)
+        assert all(0 <= r < S_q for r in rows) and rows == sorted(set(rows))
+
+
+def test_counter_summary_clock_and_busy_fractions(tmp_path, capsys):
+    """GRBM_COUNT summed over 8 XCDs over a 1 ms dispatch of 1.5e6 cycles per
+    XCD is a 1500 MHz clock; the MFMA busy and MOPS counters turn into the
+    pipe's busy fraction and the rate against the peak at that clock."""
+    d = tmp_path / "pmc"
+    os.makedirs(d / "host")
+    with open(d / "host" / "p_agent_info.csv", "w") as f:
+        f.write("Agent_Type,Num_Xcc,Simd_Count,Array_Count\nCPU,1,0,0\nGPU,8,1024,32\n")
+    cycles = 1.5e6
+    counters = {"GRBM_COUNT": 8 * cycles, "GRBM_GUI_ACTIVE": 8 * cycles * 0.9,
+                "SQ_VALU_MFMA_BUSY_CYCLES": 1024 * cycles * 0.5,
+                "SQ_BUSY_CYCLES": 32 * cycles * 0.8,
+                "SQ_INSTS_VALU_MFMA_MOPS_BF16": 1024 * cycles * 0.5 * 2}
+    with open(d / "host" / "p_counter_collection.csv", "w") as f:
+        f.write(HEADER)
+        for disp in (1, 2):
+            for name, value in counters.items():
+                f.write(f'{disp},{disp},"Agent 1",1,1,1,64,1,"attn_fwd_fast16",64,0,0,8,0,8,'
+                        f'"{name}",{value},0,1000000\n')
+    assert bench.counter_summary(str(d), skip=1) == 0
+    r = json.loads(capsys.readouterr().out)["attn_fwd_fast16"]
+    assert r["dispatches"] == 1 and r["mean_ns"] == 1000000
+    assert r["clock_mhz"] == pytest.approx(1500.0)
+    assert r["gui_active"] == pytest.approx(0.9)
+    assert r["mfma_busy"] == pytest.approx(0.5)
+    assert r["sq_busy"] == pytest.approx(0.8)
+    # half of 1024 SIMDs x 1024 FLOP/clk at 1.5 GHz
+    assert r["mfma_tflops_bf16"] == pytest.approx(1024 * 1024 * 1.5e9 * 0.5 / 1e12, rel=1e-3)
+    assert r["pct_of_bf16_peak_at_clock"] == pytest.approx(50.0 * 2516.6 / 2516.58, rel=1e-3)

@@ -6,10 +6,12 @@ max absolute error over every active output element:
   O:   1e-4 for f32 inputs, 2e-2 for bf16/f16 inputs (the target's bar);
   LSE: 1e-4 for f32 inputs, 1e-3 for bf16/f16 inputs (our own choice: the
        LSE only sees f32 score/sum rounding, so it is far tighter than O).
-Full-size workloads compare a row sample (every 16th row, rows 0, 1, S_q-1,
-and both sides of every 128-row block boundary); rows are independent, so
-each sampled row is an exact check.  The 16-bit workloads of up to 2^31
-query-key pairs are also checked on every row.
+Full-size workloads compare a row sample (every 17th row, which visits all
+32 row positions of a wave, rows 0, 1, S_q-1, and both sides of every
+128-row block boundary); rows are independent, so each sampled row is an
+exact check.  The 16-bit workloads of up to 2^31 query-key pairs, and the
+long-sequence causal workload with the wide score spread, are also checked
+on every row.
 """
 import math
 
@@ -96,6 +98,21 @@ def test_workload_every_row(name):
     o, lse = run_gpu(q, k, v, w.scale, w.causal)
     o_ref, lse_ref = run_oracle(q, k, v, w.scale, w.causal)
     check(to_np(o), to_np(lse), o_ref, lse_ref, w.dtype, f"{name} (every row)")
+
+
+def test_long_causal_wide_spread_every_row():
+    """bf16 causal, 1 x 32 x 16384 x 128 with Q, K ~ N(0, 3): every one of
+    the 524288 output rows against the oracle (about 2.2e12 fp64 FLOP on the
+    host, 20-45 s).  Its peaked rows stress the running max hardest."""
+    name = "bf16_b1h32_s16384_d128_causal_var3"
+    w = WORKLOADS[name]
+    print(f"[case] {name} (every row)", flush=True)
+    q, k, v = make_inputs(w)
+    o, lse = run_gpu(q, k, v, w.scale, w.causal)
+    o_np, lse_np = to_np(o), to_np(lse)
+    del o, lse
+    o_ref, lse_ref = run_oracle(q, k, v, w.scale, w.causal)
+    check(o_np, lse_np, o_ref, lse_ref, w.dtype, f"{name} (every row)")
 
 
 # ------------------------------------------------------------- edge cases

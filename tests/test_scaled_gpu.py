@@ -90,6 +90,57 @@ def test_scaled_special_blocks(qk):
         check(to_np(o), to_np(lse), o_ref, lse_ref, f"special blocks {qk} c={causal}")
 
 
+NEG_CASES = [
+    # B, H, S_q, S_k, D_qk, D_v, q_block, k_block
+    (1, 2, 400, 700, 128, 128, 100, 64),
+    (2, 2, 257, 513, 64, 64, 64, 128),
+    (1, 3, 300, 1000, 128, 128, 128, 192),
+]
+
+
+@pytest.mark.parametrize("qk", ["fp8_e4m3", "bf16", "f16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("pattern", ["all_negative", "mixed", "alternating_zero"])
+@pytest.mark.parametrize("case", NEG_CASES, ids=[case_id(c) for c in NEG_CASES])
+def test_scaled_negative_key_scales(case, pattern, causal, qk):
+    """Key-block scales of either sign (the per-key scale of the definition
+    has no sign premise): all negative, a seeded random mix of signs (with
+    negative query scales too), and signs alternating with zero scales, so
+    that consecutive key tiles switch sign."""
+    B, H, S_q, S_k, D_qk, D_v, qb, kb = case
+    vdt = "f16" if qk == "f16" else "bf16"
+    print(f"[case] negative key scales {case_id(case)} {pattern} causal={causal} qk={qk}",
+          flush=True)
+    q, k, v, qs, ks = scaled_inputs(B, H, S_q, S_k, D_qk, D_v, qb, kb, qk, vdt,
+                                    seed=7500 + S_q + S_k, scale_jitter=True)
+    g = torch.Generator(device="cpu").manual_seed(7600 + S_k)
+    if pattern == "all_negative":
+        ks = -ks
+    elif pattern == "mixed":
+        ks = ks * torch.where(torch.rand(ks.shape, generator=g) < 0.5, -1.0, 1.0)
+        qs = qs * torch.where(torch.rand(qs.shape, generator=g) < 0.3, -1.0, 1.0)
+    else:
+        sign = torch.tensor([1.0, -1.0, 0.0, -1.0]).repeat(ks.shape[-1] // 4 + 1)
+        ks = ks * sign[: ks.shape[-1]]
+    ks, qs = ks.contiguous(), qs.contiguous()
+    o, lse = run(q, k, v, qs, ks, qb, kb, causal)
+    o_ref, lse_ref = ref(q, k, v, qs, ks, qb, kb, causal)
+    check(to_np(o), to_np(lse), o_ref, lse_ref,
+          f"negative key scales {case_id(case)} {pattern} c={causal} {qk}")
+
+
+def test_scaled_negated_key_scales_mirror_the_scores():
+    """K_scale -> -K_scale gives the attention of -K with the original
+    scales: the same scores with their sign flipped, computed two ways."""
+    B, H, S, D, qb, kb = 1, 2, 500, 128, 128, 64
+    q, k, v, qs, ks = scaled_inputs(B, H, S, S, D, D, qb, kb, "bf16", "bf16", seed=81,
+                                    scale_jitter=True)
+    for causal in (False, True):
+        o1, l1 = run(q, k, v, qs, -ks, qb, kb, causal)
+        o2, l2 = run(q, -k, v, qs, ks, qb, kb, causal)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"causal={causal}"
+
+
 def test_scaled_matches_plain_attention():
     """16-bit Q/K with Q_scale = scale * log2(e) and K_scale = 1 is the plain
     attention of attn_fwd (the same kernel decisions, base 2 either way): the
@@ -129,7 +180,7 @@ def test_scaled_fp8_full_size(causal):
     B, H, S, D = 1, 32, 16384, 128
     q, k, v, qs, ks = scaled_inputs(B, H, S, S, D, D, 128, 64, "fp8_e4m3", "bf16", seed=80)
     o, lse = run(q, k, v, qs, ks, 128, 64, causal)
-    rows = sample_rows(S)[::4]
+    rows = sample_rows(S, stride=67)   # 67 is coprime with 32: every row position of a wave
     o_s, l_s = to_np(o[:, :, rows]), to_np(lse[:, :, rows])
     del o, lse
     o_ref, lse_ref = ref(q, k, v, qs, ks, 128, 64, causal, rows=rows)

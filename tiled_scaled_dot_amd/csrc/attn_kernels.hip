@@ -717,20 +717,8 @@ struct FastShape {
     int vslots;   // V ring size
     int occ;      // waves per SIMD the kernel is compiled for
 };
-#ifndef TSD_WIDE_KSLOTS
-#define TSD_WIDE_KSLOTS 4
-#endif
-#ifndef TSD_WIDE_VSLOTS
-#define TSD_WIDE_VSLOTS 2
-#endif
-#ifndef TSD_NARROW_KSLOTS
-#define TSD_NARROW_KSLOTS 2
-#endif
-#ifndef TSD_NARROW_VSLOTS
-#define TSD_NARROW_VSLOTS 2
-#endif
-constexpr FastShape kShapeWide = {8, TSD_WIDE_KSLOTS, TSD_WIDE_VSLOTS, 2};
-constexpr FastShape kShapeNarrow = {4, TSD_NARROW_KSLOTS, TSD_NARROW_VSLOTS, 3};
+constexpr FastShape kShapeWide = {8, 4, 2, 2};
+constexpr FastShape kShapeNarrow = {4, 2, 2, 3};
 constexpr FastShape fast_shape(int dq, int dv)
 {
     return (dq <= 64 && dv <= 64) ? kShapeNarrow : kShapeWide;
@@ -761,24 +749,12 @@ __host__ __device__ __attribute__((always_inline)) inline void static_for(F &&f)
 // pipes taking turns.  These scheduling groups ask for each MFMA to be
 // followed by a few VALU instructions and the next LDS reads, keeping
 // operands a few reads ahead.  Masks: 0x8 MFMA, 0x2 VALU, 0x100 LDS read.
-#ifndef TSD_SCHED
-#define TSD_SCHED 1
-#endif
-#ifndef TSD_SCHED_VALU
-#define TSD_SCHED_VALU 3
-#endif
-#ifndef TSD_SCHED_LEAD
-#define TSD_SCHED_LEAD 4
-#endif
-#ifndef TSD_DMA_LEAD
-#define TSD_DMA_LEAD 1
-#endif
-#ifndef TSD_BAR2
-#define TSD_BAR2 1
-#endif
-#ifndef TSD_SCHED_VALU8
-#define TSD_SCHED_VALU8 4   // VALU slots per fp8 score MFMA, in units of TSD_SCHED_VALU
-#endif
+constexpr int kSchedValu = 3;    // VALU slots per MFMA (128-wide Q/K; 64-wide: one more)
+constexpr int kSchedLead = 4;    // LDS operand reads issued ahead of their MFMA
+constexpr int kSchedValu8 = 4;   // VALU slots per fp8 score MFMA, in units of kSchedValu
+// Causal launches of the 8-wave shape synchronise every second key tile
+// (four-tile V ring).
+constexpr bool kBar2 = true;
 template <int MASK, int N>
 __device__ __attribute__((always_inline)) inline void sched_group()
 {
@@ -790,11 +766,11 @@ __device__ __attribute__((always_inline)) inline void sched_group()
 // (two transposed V reads and VA VALU slots each).  VA is 3 for 128-wide
 // Q/K and 4 for 64-wide Q/K, whose tiles have half the score MFMAs for the
 // same softmax work.
-template <int NS, int NP, int RS = 1, int VS = 1, int VA = TSD_SCHED_VALU>
+template <int NS, int NP, int RS = 1, int VS = 1, int VA = kSchedValu>
 __device__ __attribute__((always_inline)) inline void schedule_iteration()
 {
-    if constexpr (TSD_SCHED) {
-        constexpr int LEAD = TSD_SCHED_LEAD < NS * RS ? TSD_SCHED_LEAD : NS * RS;
+    {
+        constexpr int LEAD = kSchedLead < NS * RS ? kSchedLead : NS * RS;
         sched_group<0x100, LEAD>();
         sched_group<0x002, 2 * VA>();
         static_for<0, NS>([&](auto ic) __attribute__((always_inline)) {
@@ -832,7 +808,7 @@ struct Fast16 {
     // ahead in issue priority, and reaches the barrier ~600 clocks before
     // the second; this way the second starts its MFMAs right after the
     // barrier instead of issuing loads.
-    static constexpr int DMA_WAVES = (TSD_DMA_LEAD && NW == 8) ? NW / 2 : NW;
+    static constexpr int DMA_WAVES = NW == 8 ? NW / 2 : NW;
     static constexpr int K_PER_W = KT / 1024 / DMA_WAVES;   // 1 KB loads per issuing wave
     static constexpr int V_PER_W = VT / 1024 / DMA_WAVES;
     static constexpr int LOADS = K_PER_W + V_PER_W;  // per issuing wave per tile
@@ -939,7 +915,7 @@ attn_fwd_fast16(KernelArgs p)
     // Causal attention with the 8-wave shape synchronises every second key
     // tile (measured 1-3% faster there, 1% slower without the causal mask;
     // the per-block scaled kernels would spill).
-    constexpr bool BAR2 = TSD_BAR2 && CAUSAL && !SCALED && fast_shape(DQ, DV).kslots == 4;
+    constexpr bool BAR2 = kBar2 && CAUSAL && !SCALED && fast_shape(DQ, DV).kslots == 4;
     using T = Fast16<DQ, DV, QK8 ? 1 : 2, BAR2>;
     constexpr int BN = T::BN;
     constexpr int QKB = QK8 ? 1 : 2;          // bytes per Q/K element
@@ -1254,17 +1230,39 @@ attn_fwd_fast16(KernelArgs p)
     f32x16 sc[2][2];     // scores of tiles t and t+1, alternating by parity
     float mxs[2];        // their row maxima (both lane halves)
     bool grows[2];       // some row's max exceeds m by more than 2^kTau (unmasked tiles)
-    // SCALED: the key block scale of tile t (wave-uniform, a scalar load).
-    // Scales are >= 0, so the max of the scaled scores is the scale times
-    // the max of the raw ones; a zero scale is raised to the smallest normal
-    // float, which keeps masked scores at -inf and changes no result.
+    // SCALED: the key block scale of tile t (wave-uniform, a scalar load),
+    // read one tile ahead of its use.  The scores of a tile whose key scale
+    // is negative are formed with -Q (a sign flip of the Q fragment, exact),
+    // so the scale applied to every tile's raw scores is |K_scale| > 0: the
+    // max of the scaled scores is that scale times the max of the raw ones
+    // and masked scores stay -inf.  A zero scale is raised to the smallest
+    // normal float, which changes no result.
     float kss[2] = {1.0f, 1.0f};
+    float ks_ahead = 0.0f;   // key scale of the tile after the next one
+    bool q_neg = false;      // the Q fragment holds -Q
     auto key_scale = [&](int t) __attribute__((always_inline)) {
         const int tt = min(t, ntiles - 1);
-        const float v = p.K_scale[(size_t)slice * p.k_scale_blocks + tt / p.k_tiles_per_block];
-        return fmaxf(v, 1.17549435e-38f);
+        return p.K_scale[(size_t)slice * p.k_scale_blocks + tt / p.k_tiles_per_block];
     };
-    if constexpr (SCALED) kss[0] = key_scale(0);
+    auto key_mag = [](float ks) __attribute__((always_inline)) {
+        return fmaxf(__builtin_fabsf(ks), 1.17549435e-38f);
+    };
+    // the sign of Q for the scores of a tile with key scale ks (wave-uniform)
+    auto key_sign = [&](float ks) __attribute__((always_inline)) {
+        const bool neg = ks < 0.0f;
+        if (neg != q_neg) {
+            constexpr uint32_t flip = QK8 ? 0x80808080u : 0x80008000u;
+#pragma unroll
+            for (int j = 0; j < QCH; ++j) qf[j] ^= flip;
+            q_neg = neg;
+        }
+    };
+    if constexpr (SCALED) {
+        const float ks0 = key_scale(0);
+        key_sign(ks0);
+        kss[0] = key_mag(ks0);
+        ks_ahead = key_scale(1);
+    }
     scores(0, sc[0]);
     mxs[0] = max_halves(lane_max(sc[0]));
     if constexpr (SCALED) mxs[0] *= kss[0];
@@ -1289,7 +1287,12 @@ attn_fwd_fast16(KernelArgs p)
 
         float mx = mxs[u & 1];
         bool grow_any = grows[u & 1];
-        if constexpr (SCALED) kss[(u + 1) & 1] = key_scale(t + 1);
+        if constexpr (SCALED) {
+            // tile t+1: its scale was read during the previous iteration
+            key_sign(ks_ahead);
+            kss[(u + 1) & 1] = key_mag(ks_ahead);
+            ks_ahead = key_scale(t + 2);
+        }
         if (active) {
             // masks: keys >= S_k; keys after the query when causal (in the
             // extended kernel: keys outside the row's [lo_i, hi_i))
@@ -1387,7 +1390,9 @@ attn_fwd_fast16(KernelArgs p)
         float rs = 0.0f;
         u32x4 pb0[2], pb1[2];
         float ct = c;   // exponent factor of this tile's raw scores
-        if constexpr (SCALED) ct = c * kss[u & 1];
+        // (raised to the smallest normal float: a product that underflows
+        // to 0 would turn the -inf of a masked score into NaN)
+        if constexpr (SCALED) ct = fmaxf(c * kss[u & 1], 1.17549435e-38f);
         // phase A: scores of tile t+1 (garbage past the last tile, unused) || P of block 0
         scores(so1, sn);
         probs(s[0], ct, mc, pb0, rs);
@@ -1403,10 +1408,10 @@ attn_fwd_fast16(KernelArgs p)
         grows[(u + 1) & 1] = __builtin_amdgcn_ballot_w64((mxs[(u + 1) & 1] - m) * c > kTau) != 0;
         l += rs;
         if constexpr (QK8)
-            schedule_iteration<2 * (DQ / 64), 4 * (DV / 32), 2, TSD_SCHED_VALU8>();
+            schedule_iteration<2 * (DQ / 64), 4 * (DV / 32), 2, kSchedValu8>();
         else
             schedule_iteration<2 * (DQ / 16), 4 * (DV / 32), 1, 1,
-                               DQ <= 64 ? TSD_SCHED_VALU + 1 : TSD_SCHED_VALU>();
+                               DQ <= 64 ? kSchedValu + 1 : kSchedValu>();
     };
 
     for (int t0 = 0; t0 < ntiles; t0 += T::U) {
@@ -1969,9 +1974,8 @@ hipError_t dispatch_causal(int dtype, bool causal, int64_t grid, const KernelArg
 }  // namespace
 
 #if TSD_UNIT == 0
-#ifndef TSD_SPLIT_BELOW
-#define TSD_SPLIT_BELOW 512
-#endif
+// f32 grids below this many 128-row blocks take the key-split kernel.
+constexpr int64_t kSplitBelow = 512;
 TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec, int64_t slices,
                        int64_t S_q, bool causal)
 {
@@ -1983,14 +1987,14 @@ TileConfig tile_config(int dtype, int64_t D_qk, int64_t D_v, bool vec, int64_t s
     // launch fewer than two per CU, the key-split kernel (32 rows per
     // workgroup) spreads the work over four times as many.
     t.split_keys = dtype == TSD_F32 && slices > 0 &&
-                   slices * ((S_q + kBlockM - 1) / kBlockM) < TSD_SPLIT_BELOW;
+                   slices * ((S_q + kBlockM - 1) / kBlockM) < kSplitBelow;
     if (t.fast) {
         const FastShape sh = fast_shape(t.dqk_block, t.dv_block);
         t.block_m = 32 * sh.waves;
         t.waves = sh.waves;
         t.threads = 64 * sh.waves;
         t.block_n = 64;
-        const int vslots = (TSD_BAR2 && causal && sh.kslots == 4) ? 4 : sh.vslots;
+        const int vslots = (kBar2 && causal && sh.kslots == 4) ? 4 : sh.vslots;
         t.lds_bytes = (sh.kslots * t.dqk_block + vslots * t.dv_block) * 64 * 2;
     } else if (t.split_keys) {
         // widths padded to 64, 96 or 128 (MFMA work grows with the padding)

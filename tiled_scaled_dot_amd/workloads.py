@@ -323,9 +323,14 @@ def scaled_inputs(B, H, S_q, S_k, D_qk, D_v, q_block, k_block, qk_dtype: str, v_
     return q, k, v.to(DTYPES[v_dtype]), q_scale.float().contiguous(), k_scale.float().contiguous()
 
 
-def sample_rows(S_q: int, block_m: int = 128, stride: int = 16):
+def sample_rows(S_q: int, block_m: int = 128, stride: int = 17):
     """Query rows checked at full size: every `stride`-th row, rows 0, 1,
-    S_q-1, and the rows on both sides of every `block_m` boundary."""
+    S_q-1, and the rows on both sides of every `block_m` boundary.
+
+    The default stride, 17, is coprime with 32, the query rows one wave of
+    the kernels owns: over any 32 * 17 consecutive rows the stride-17 rows
+    take every position 0..31 within their wave, so a fault tied to one lane
+    position is not skipped."""
     rows = set(range(0, S_q, stride))
     rows.update({0, 1, S_q - 1})
     for b in range(block_m, S_q, block_m):
