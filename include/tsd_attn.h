@@ -49,7 +49,9 @@ enum {
     TSD_ERR_SCALE = 4,       /* scale is NaN or infinite                        */
     TSD_ERR_ALIAS = 5,       /* O or LSE overlaps Q, K, V, or each other (the
                                 output region must be disjoint from the inputs) */
-    TSD_ERR_HIP = 6          /* the kernel launch itself failed                 */
+    TSD_ERR_HIP = 6,         /* the kernel launch itself failed                 */
+    TSD_ERR_SCRATCH = 7      /* attn_fwd_splitkv_noalloc: the partial results
+                                exceed TSD_NOALLOC_SCRATCH_BYTES                */
 };
 
 /* Storage dtypes of Q, K, V and O (all four share one).  Accumulation is
@@ -276,6 +278,30 @@ TSD_API int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *
                              int64_t D_qk, int64_t D_v, float scale, int causal, int dtype,
                              const tsd_mask *mask, int64_t n_splits,
                              void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_splitkv_noalloc — attn_fwd_splitkv for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace.  The partial results are staged in a scratch array of
+ * TSD_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on until the process ends (the device is the current one, which must be
+ * the device of `stream`).  The call allocates nothing and frees nothing.
+ *   - A plan whose workspace (attn_splitkv_plan) exceeds the array:
+ *     TSD_ERR_SCRATCH, nothing launched.  One chunk needs no scratch.
+ *   - All calls on one device share its array.  Calls that overlap in time
+ *     on one device (other streams, other host threads) race on it and give
+ *     wrong results: serialise them (one stream, or events).  Each call
+ *     writes every scratch entry it reads, so nothing carries over from an
+ *     earlier call.
+ * Other statuses, results and threading as for attn_fwd_splitkv.
+ */
+#define TSD_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)   /* 64 MiB */
+TSD_API int attn_fwd_splitkv_noalloc(const void *Q, const void *K, const void *V, void *O,
+                                     float *LSE, int64_t B, int64_t H, int64_t H_kv,
+                                     int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
+                                     float scale, int causal, int dtype,
+                                     const tsd_mask *mask, int64_t n_splits, void *stream);
 
 /*
  * attn_fwd_scaled — base-2 attention with per-block Q and K scales

@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert tsd.attn_status_string(code)
     assert tsd.attn_status_string(99) == "unknown status"
 
@@ -365,6 +365,26 @@ def test_splitkv_workspace_checks(lib):
     assert tsd.attn_fwd_splitkv_raw(*args, 0x60000000 + 64, ws) == 3  # not 256-aligned
     assert tsd.attn_fwd_splitkv_raw(*args, OA, ws) == 5             # workspace on O
     assert tsd.attn_fwd_splitkv_raw(*args, KA - 256, ws) == 5       # workspace into K
+
+
+def test_splitkv_noalloc_host_checks(lib):
+    """attn_fwd_splitkv_noalloc rejects, before any HIP call, what
+    attn_fwd_splitkv rejects, and a plan whose partial results exceed the
+    fixed scratch array with TSD_ERR_SCRATCH."""
+    call = tsd.attn_fwd_splitkv_noalloc_raw
+    good = (QA, KA, VA, OA, LA, 1, 2, 2, 128, 4096, 64, 64, 0.125, 0, 2, None, 4)
+    assert call(None, *good[1:]) == 1
+    assert call(*good[:3], None, *good[4:]) == 1
+    assert call(*good[:14], 0, None, 4) == 3                         # f32: fast path only
+    assert call(*good[:3], OA + 8, *good[4:]) == 3                   # O not 16-byte aligned
+    assert call(*good[:15], MK(4096, kv_begin=-1), 4) == 2
+    assert call(*good[:16], 300) == 3                                # more than 256 chunks
+    # 64 heads x 4096 rows x 128 f32 columns x 64 chunks: 8 GiB of partials
+    n, _, ws = tsd.attn_splitkv_plan(1, 64, 4096, 65536, 128, 128, False, "bf16", None, 64)
+    assert n == 64 and ws > tsd.NOALLOC_SCRATCH_BYTES
+    assert call(QA, KA, VA, OA, LA, 1, 64, 64, 4096, 65536, 128, 128, 0.125, 0, 2, None,
+                64) == 7
+    assert "scratch" in tsd.attn_status_string(7)
 
 
 def test_planner_and_checks_from_many_threads(lib):

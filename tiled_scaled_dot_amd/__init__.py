@@ -13,7 +13,8 @@ import os
 
 __all__ = ["attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string",
            "attn_fwd_ext", "attn_fwd_partial", "attn_merge", "attn_splitkv_plan",
-           "attn_fwd_splitkv", "attn_fwd_scaled", "TsdMask", "TsdError", "library",
+           "attn_fwd_splitkv", "attn_fwd_splitkv_noalloc", "attn_fwd_scaled", "TsdMask",
+           "TsdError", "library", "NOALLOC_SCRATCH_BYTES",
            "LIBRARY_PATH",
            "DTYPE_CODES", "STATUS"]
 
@@ -27,12 +28,14 @@ STATUS = {
     4: "TSD_ERR_SCALE",
     5: "TSD_ERR_ALIAS",
     6: "TSD_ERR_HIP",
+    7: "TSD_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20   # TSD_NOALLOC_SCRATCH_BYTES of the C header
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2, "fp8_e4m3": 3}
 
 EXPORTED = ("attn_fwd", "attn_fwd_plan", "attn_fwd_plan_block", "attn_status_string",
             "attn_fwd_ext", "attn_fwd_partial", "attn_merge", "attn_splitkv_plan",
-            "attn_fwd_splitkv", "attn_fwd_scaled")
+            "attn_fwd_splitkv", "attn_fwd_scaled", "attn_fwd_splitkv_noalloc")
 
 
 class TsdError(RuntimeError):
@@ -124,6 +127,9 @@ def library(path: str = LIBRARY_PATH) -> ctypes.CDLL:
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, f,
                                      ci, ci, mp, i64, vp, i64, vp]
     lib.attn_fwd_splitkv.restype = ci
+    lib.attn_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                             i64, f, ci, ci, mp, i64, vp]
+    lib.attn_fwd_splitkv_noalloc.restype = ci
     lib.attn_fwd_scaled.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                                     i64, i64, ci, ci, ci, vp]
     lib.attn_fwd_scaled.restype = ci
@@ -349,6 +355,37 @@ def attn_fwd_splitkv(q, k, v, scale=None, causal=False, causal_offset=0, window=
                                 lse.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
                                 code, mask, n_splits, ws_ptr, ws_bytes,
                                 _stream(stream, q.device)))
+    return out, lse
+
+
+def attn_fwd_splitkv_noalloc_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, H_kv, S_q, S_k,
+                                 D_qk, D_v, scale, causal, dtype, mask, n_splits,
+                                 stream=None) -> int:
+    return library().attn_fwd_splitkv_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, H_kv,
+                                              S_q, S_k, D_qk, D_v, float(scale),
+                                              int(bool(causal)), _code(dtype), _mask_ref(mask),
+                                              n_splits, stream)
+
+
+def attn_fwd_splitkv_noalloc(q, k, v, scale=None, causal=False, causal_offset=0, window=0,
+                             kv_begin=0, kv_end=None, n_splits=0, out=None, lse=None,
+                             stream=None):
+    """attn_fwd_splitkv with the partial results in the library's fixed
+    per-device scratch array (NOALLOC_SCRATCH_BYTES): the library allocates
+    nothing.  Pass ``out`` and ``lse`` to allocate nothing here either.
+    Calls that overlap on one GPU share the array and race."""
+    import torch
+
+    code, B, H, H_kv, S_q, S_k, D_qk, D_v = _qkv(q, k, v, grouped=True)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D_qk)
+    out = _buffer(out, (B, H, S_q, D_v), q.dtype, q, "out")
+    lse = _buffer(lse, (B, H, S_q), torch.float32, q, "lse")
+    mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
+    _check(attn_fwd_splitkv_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        out.data_ptr(), lse.data_ptr(), B, H, H_kv, S_q, S_k,
+                                        D_qk, D_v, scale, causal, code, mask, n_splits,
+                                        _stream(stream, q.device)))
     return out, lse
 
 

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "launch.h"
 #include "tsd_attn.h"
@@ -502,6 +503,71 @@ extern "C" int attn_fwd_splitkv(const void *Q, const void *K, const void *V, voi
     return attn_merge(o_parts, l_parts, n, B, H, S_q, D_v, O, LSE, dtype, stream);
 }
 
+// ------------------------------------------------------------------------
+// attn_fwd_splitkv_noalloc: the split-KV path with its partial results in a
+// fixed device array instead of a caller workspace.  The array is a
+// file-scope __device__ object: the loader places one copy on every device
+// the library runs on, each held until the process ends.  In host code its
+// name stands for a host-side shadow, not a device address, so the device
+// address of the current device's copy is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+namespace {
+
+__device__ __align__(256) uint8_t scratch[TSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
+
+// Device address of the current device's scratch array.
+int scratch_address(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TSD_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return TSD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TSD_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TSD_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd_splitkv_noalloc(const void *Q, const void *K, const void *V, void *O,
+                                        float *LSE, int64_t B, int64_t H, int64_t H_kv,
+                                        int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
+                                        float scale, int causal, int dtype,
+                                        const tsd_mask *mask, int64_t n_splits, void *stream)
+{
+    const ExtShape es{B, H, H_kv, S_q, S_k, D_qk, D_v};
+    int st = check_ext_inputs(Q, K, V, es, scale, dtype);
+    if (st != TSD_OK) return st;
+    if (!O) return TSD_ERR_NULL;
+    tsd_mask mk;
+    if ((st = check_mask(mask, S_k, &mk)) != TSD_OK) return st;
+    int64_t n = 0, len = 0, ws = 0;
+    if ((st = splitkv_plan(es, causal, dtype, mk, n_splits, &n, &len, &ws)) != TSD_OK)
+        return st;
+    if (n == 1)   // one chunk: no partial results, nothing staged
+        return attn_fwd_ext(Q, K, V, O, LSE, B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
+                            dtype, &mk, stream);
+    if (ws > TSD_NOALLOC_SCRATCH_BYTES) return TSD_ERR_SCRATCH;
+    if ((uintptr_t)O % 16 != 0 || (uintptr_t)LSE % 4 != 0) return TSD_ERR_UNSUPPORTED;
+    void *work = nullptr;
+    if ((st = scratch_address(&work)) != TSD_OK) return st;
+    // The same chunking, so attn_fwd_splitkv takes the same plan and checks
+    // the outputs against the scratch array like any workspace.  Every
+    // partial entry is written before the merge reads it (chunks a row sees
+    // nothing of get O = 0, LSE = -inf), so nothing left from an earlier
+    // call is read.
+    return attn_fwd_splitkv(Q, K, V, O, LSE, B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
+                            dtype, &mk, n, work, TSD_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 extern "C" int attn_fwd_scaled(const void *Q, const void *K, const void *V, void *O, float *LSE,
                                const float *Q_scale, const float *K_scale, int64_t B,
                                int64_t H, int64_t S_q, int64_t S_k, int64_t D_qk, int64_t D_v,
@@ -570,6 +636,9 @@ extern "C" const char *attn_status_string(int status)
     case TSD_ERR_SCALE: return "scale is not finite";
     case TSD_ERR_ALIAS: return "output buffer overlaps an input or the other output";
     case TSD_ERR_HIP: return "HIP kernel launch failed";
+    case TSD_ERR_SCRATCH:
+        return "the partial results need more than the library's fixed scratch array "
+               "(TSD_NOALLOC_SCRATCH_BYTES); use attn_fwd_splitkv with a workspace";
     default: return "unknown status";
     }
 }
