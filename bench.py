@@ -63,6 +63,11 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps launches of a plain device "
                          "copy of this many MiB (counter calibration for HBM traffic)")
+    ap.add_argument("--gemm-probe", type=int, default=0, metavar="N",
+                    help="instead of the benchmark, run --steps bf16 N x N x N matrix products "
+                         "(torch.matmul, the platform's GEMM library) after the clock settle "
+                         "and print their rate: the MFMA rate a plain dense contraction "
+                         "sustains on this GPU, for comparison")
     ap.add_argument("--record-traffic", nargs=4, metavar=("ATTN_FETCH", "ATTN_WRITE",
                                                           "COPY_FETCH", "COPY_WRITE"),
                     help="write the HBM traffic per launch into the stored traffic record "
@@ -76,6 +81,12 @@ def parse():
                          "fraction and the rate against the peak at that clock")
     ap.add_argument("--skip-dispatches", type=int, default=0,
                     help="--counter-summary: leave out the first N dispatches (clock ramp)")
+    ap.add_argument("--trace-summary", metavar="FOLDER",
+                    help="instead of the benchmark, summarise a rocprofv3 --kernel-trace folder: "
+                         "per kernel, the dispatch count and the mean duration over all "
+                         "dispatches and over the last --last (the back-to-back block)")
+    ap.add_argument("--last", type=int, default=50,
+                    help="--trace-summary: dispatches at the end of the trace to average")
     return ap.parse_args()
 
 
@@ -124,6 +135,37 @@ def copy_probe(mib: int, launches: int) -> int:
         dst.copy_(src[:, :cols])
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes": rows * cols * 4, "launches": launches}), flush=True)
+    return 0
+
+
+def gemm_probe(n: int, launches: int, settle_s: float) -> int:
+    """Time `launches` bf16 n x n x n products C = A B (torch.matmul, which
+    calls the platform GEMM library) back to back between two events, after
+    running them for `settle_s` seconds; print the rate and its fraction of
+    the dense bf16 peak."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(0)
+    a = torch.randn((n, n), generator=g).to(dev, torch.bfloat16)
+    b = torch.randn((n, n), generator=g).to(dev, torch.bfloat16)
+    c = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(launches):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    print(json.dumps({"gemm_probe": f"bf16 {n}x{n}x{n}", "launches": launches, "ms": round(ms, 4),
+                      "tflops": round(tflops, 1),
+                      "frac_of_dense_bf16_peak": round(tflops / PEAK_TFLOPS["bf16"], 4)}),
+          flush=True)
     return 0
 
 
@@ -265,6 +307,37 @@ def counter_summary(folder: str, skip: int = 0) -> int:
     return 0
 
 
+def trace_summary(folder: str, last: int) -> int:
+    """Per kernel of a rocprofv3 --kernel-trace folder (csv output): the
+    dispatch count, mean / min / max duration over all dispatches, and the
+    mean over the last `last` dispatches, which for a bench.py run are the
+    back-to-back block it times for the roofline."""
+    import csv
+    import glob
+
+    per = {}
+    for path in glob.glob(os.path.join(folder, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                per.setdefault(row["Kernel_Name"], []).append(
+                    (int(row["Start_Timestamp"]), int(row["End_Timestamp"]) - int(row["Start_Timestamp"]),
+                     int(row.get("Grid_Size_X", row.get("Grid_Size", 0)) or 0),
+                     int(row.get("Workgroup_Size_X", row.get("Workgroup_Size", 0)) or 0)))
+    if not per:
+        raise SystemExit(f"no kernel trace rows in {folder}")
+    result = {}
+    for kernel, ds in per.items():
+        ds.sort()
+        ns = [d[1] for d in ds]
+        tail = ns[-last:] if last > 0 else ns
+        result[kernel] = {"dispatches": len(ns), "mean_ns": round(sum(ns) / len(ns)),
+                          "min_ns": min(ns), "max_ns": max(ns),
+                          f"mean_ns_last_{len(tail)}": round(sum(tail) / len(tail)),
+                          "workgroups": ds[0][2] // max(ds[0][3], 1), "threads": ds[0][3]}
+    print(json.dumps(result, indent=1))
+    return 0
+
+
 def cpu_baseline(w, q, k, v, stride: int, scales=None):
     import numpy as np
 
@@ -325,8 +398,12 @@ def main():
         return record_traffic(args)
     if args.counter_summary:
         return counter_summary(args.counter_summary, args.skip_dispatches)
+    if args.trace_summary:
+        return trace_summary(args.trace_summary, args.last)
     if args.copy_probe_mib:
         return copy_probe(args.copy_probe_mib, args.steps)
+    if args.gemm_probe:
+        return gemm_probe(args.gemm_probe, args.steps, args.settle_s)
 
     import torch
 

@@ -304,32 +304,19 @@ def load_page_example():
 
 
 def _page_order_f32(q, k, v, scale):
-    """The page's own float32 check, step by step: scores, max from -inf,
-    shifted exp sum, then weight = exp / denominator times the value."""
-    q, k, v = (x.astype(np.float32) for x in (q, k, v))
-    out = np.zeros((q.shape[0], q.shape[1], v.shape[2]), dtype=np.float32)
-    sc = np.float32(scale)
-    for b in range(q.shape[0]):
-        for i in range(q.shape[1]):
-            scores = []
-            for j in range(k.shape[1]):
-                dot = np.float32(0.0)
-                for d in range(q.shape[2]):
-                    dot = np.float32(dot + q[b, i, d] * k[b, j, d])
-                scores.append(np.float32(dot * sc))
-            mx = np.float32(-np.inf)
-            for s in scores:
-                mx = max(mx, s)
-            den = np.float32(0.0)
-            for s in scores:
-                den = np.float32(den + np.exp(np.float32(s - mx)))
-            for c in range(v.shape[2]):
-                acc = np.float32(0.0)
-                for j, s in enumerate(scores):
-                    w = np.float32(np.exp(np.float32(s - mx)) / den)
-                    acc = np.float32(acc + w * v[b, j, c])
-                out[b, i, c] = acc
-    return out
+    """A float32 evaluation of the chain the page's check follows, written
+    with whole-array operations: the dot products, then the scale; the row
+    max, seeded with -inf; the sum over keys of exp(score - max); each
+    weight as that exp divided by the sum; the weighted sum of the value
+    rows.  Only the rounding differs from the fp64 oracle, so the two agree
+    to the page's float32 tolerance."""
+    q32, k32, v32 = (np.asarray(x, dtype=np.float32) for x in (q, k, v))
+    scores = np.matmul(q32, np.swapaxes(k32, -1, -2)).astype(np.float32) * np.float32(scale)
+    row_max = np.max(scores, axis=-1, initial=np.float32(-np.inf), keepdims=True)
+    shifted = np.exp((scores - row_max).astype(np.float32))
+    denom = np.sum(shifted, axis=-1, keepdims=True, dtype=np.float32)
+    weights = (shifted / denom).astype(np.float32)
+    return np.matmul(weights, v32).astype(np.float32)
 
 
 def pin_page_worked_example(lib):

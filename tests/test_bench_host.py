@@ -121,3 +121,22 @@ def test_counter_summary_clock_and_busy_fractions(tmp_path, capsys):
     # half of 1024 SIMDs x 1024 FLOP/clk at 1.5 GHz
     assert r["mfma_tflops_bf16"] == pytest.approx(1024 * 1024 * 1.5e9 * 0.5 / 1e12, rel=1e-3)
     assert r["pct_of_bf16_peak_at_clock"] == pytest.approx(50.0 * 2516.6 / 2516.58, rel=1e-3)
+
+
+def test_trace_summary_back_to_back_window(tmp_path, capsys):
+    """The trace summary averages every dispatch and, separately, the last N
+    (the back-to-back block bench.py times), in start-time order."""
+    d = tmp_path / "trace" / "host"
+    os.makedirs(d)
+    with open(d / "s_kernel_trace.csv", "w") as f:
+        f.write("Kind,Dispatch_Id,Kernel_Name,Start_Timestamp,End_Timestamp,Grid_Size_X,"
+                "Workgroup_Size_X\n")
+        # rows out of order on purpose; durations 400 (first), then 100, 100, 200, 200
+        for i, (start, dur) in enumerate([(50, 200), (0, 400), (10, 100), (60, 200), (20, 100)]):
+            f.write(f"KERNEL_DISPATCH,{i},attn_fwd_fast16,{start},{start + dur},1024,512\n")
+    assert bench.trace_summary(str(tmp_path / "trace"), last=2) == 0
+    r = json.loads(capsys.readouterr().out)["attn_fwd_fast16"]
+    assert r["dispatches"] == 5 and r["mean_ns"] == 200
+    assert r["min_ns"] == 100 and r["max_ns"] == 400
+    assert r["mean_ns_last_2"] == 200
+    assert r["workgroups"] == 2 and r["threads"] == 512
