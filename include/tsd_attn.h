@@ -285,8 +285,9 @@ TSD_API int attn_fwd_splitkv(const void *Q, const void *K, const void *V, void *
  * loops, harnesses that forbid hipMalloc): the same arguments without the
  * workspace.  The partial results are staged in a scratch array of
  * TSD_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
- * on until the process ends (the device is the current one, which must be
- * the device of `stream`).  The call allocates nothing and frees nothing.
+ * on until the process ends (the device is the current one; a `stream` of
+ * another device: TSD_ERR_UNSUPPORTED).  The call allocates nothing and
+ * frees nothing.
  *   - A plan whose workspace (attn_splitkv_plan) exceeds the array:
  *     TSD_ERR_SCRATCH, nothing launched.  One chunk needs no scratch.
  *   - All calls on one device share its array.  Calls that overlap in time

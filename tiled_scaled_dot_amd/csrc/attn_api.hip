@@ -519,12 +519,19 @@ constexpr int kMaxDevices = 256;
 std::mutex g_scratch_mu;
 void *g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device
 
-// Device address of the current device's scratch array.
-int scratch_address(void **out)
+// Device address of the current device's scratch array.  The kernels run
+// on the device of `stream`: a stream of another device would get an
+// address it cannot use, so that is refused.
+int scratch_address(hipStream_t stream, void **out)
 {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return TSD_ERR_HIP;
     if (dev < 0 || dev >= kMaxDevices) return TSD_ERR_UNSUPPORTED;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return TSD_ERR_HIP;
+        if ((int)sdev != dev) return TSD_ERR_UNSUPPORTED;
+    }
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_ptr[dev]) {
         void *p = nullptr;
@@ -558,7 +565,8 @@ extern "C" int attn_fwd_splitkv_noalloc(const void *Q, const void *K, const void
     if (ws > TSD_NOALLOC_SCRATCH_BYTES) return TSD_ERR_SCRATCH;
     if ((uintptr_t)O % 16 != 0 || (uintptr_t)LSE % 4 != 0) return TSD_ERR_UNSUPPORTED;
     void *work = nullptr;
-    if ((st = scratch_address(&work)) != TSD_OK) return st;
+    if ((st = scratch_address(reinterpret_cast<hipStream_t>(stream), &work)) != TSD_OK)
+        return st;
     // The same chunking, so attn_fwd_splitkv takes the same plan and checks
     // the outputs against the scratch array like any workspace.  Every
     // partial entry is written before the merge reads it (chunks a row sees
