@@ -101,6 +101,48 @@ def test_ext_masks(case, dtype):
     check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"ext {mask_id(case)} {dtype}")
 
 
+# Slices of at most 32 query rows (decoding): one wave holds every row and
+# the others only stream tiles.  The cases put the visible keys in one half
+# of a 64-key tile (S_k or the window under 32, a key range inside one
+# half), make some rows see nothing, and cover the head widths of both
+# launch shapes.
+DECODE = [
+    # B, H, S_q, S_k, D_qk, D_v, causal, causal_offset, window, kv_begin, kv_end
+    (2, 4, 1, 1, 128, 128, True, 0, 0, 0, None),             # one key: the second half is empty
+    (2, 4, 1, 31, 128, 128, True, 30, 0, 0, None),           # keys in the first half only
+    (1, 4, 1, 33, 64, 64, True, 32, 0, 0, None),             # one key in the second half
+    (1, 4, 1, 4097, 128, 128, True, 4096, 0, 0, None),
+    (2, 3, 7, 1000, 128, 128, True, 993, 0, 0, None),
+    (1, 2, 32, 2000, 64, 64, True, 1968, 0, 0, None),        # 32 rows: the largest such slice
+    (1, 2, 31, 777, 80, 80, True, 746, 0, 0, None),          # head-width tail
+    (1, 2, 16, 900, 64, 128, True, 884, 0, 0, None),         # D_qk != D_v
+    (1, 2, 16, 900, 128, 64, False, 0, 0, 0, None),
+    (1, 2, 20, 1000, 128, 128, True, -10, 0, 0, None),       # rows 0..9 see nothing
+    (1, 2, 5, 3000, 128, 128, True, 2995, 20, 0, None),      # window inside one half
+    (1, 2, 5, 3000, 128, 128, True, 2995, 40, 0, None),      # window across both halves
+    (1, 2, 5, 3000, 64, 64, True, 2995, 1000, 0, None),
+    (1, 2, 8, 2000, 128, 128, False, 0, 0, 96, 120),          # key range in the second half
+    (1, 2, 8, 2000, 128, 128, False, 0, 0, 64, 90),           # ... in the first half
+    (1, 2, 8, 2000, 128, 128, True, 1500, 100, 130, 1900),
+    (1, 1, 4, 300, 64, 64, False, 0, 0, 64, 64),              # empty key range
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", DECODE, ids=[mask_id(c) for c in DECODE])
+def test_ext_decode_rows(case, dtype):
+    B, H, S_q, S_k, D_qk, D_v, causal, coff, window, kb, ke = case
+    print(f"[case] ext decode {mask_id(case)} {dtype}", flush=True)
+    scale = 1 / math.sqrt(D_qk)
+    q, k, v = random_inputs((B, H, S_q, D_qk), (B, H, S_k, D_qk), (B, H, S_k, D_v), dtype,
+                            seed=2500 + S_q + 3 * S_k + coff + window)
+    o, lse = tsd.attn_fwd_ext(*gpu(q, k, v), scale=scale, causal=causal, causal_offset=coff,
+                              window=window, kv_begin=kb, kv_end=ke)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_ext(q, k, v, scale, causal, coff, window, kb, ke)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"ext decode {mask_id(case)} {dtype}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 4, 1000, 777, 128, 128), (1, 2, 513, 1029, 64, 64),
                                    (2, 8, 384, 640, 64, 128), (1, 1, 1, 200, 128, 64)])
@@ -136,6 +178,8 @@ PARTIALS = [
     (1, 2, 300, 2000, 64, True, 1700, 600, 0, None, 8, 256),   # chunks empty for all rows
     (1, 2, 300, 2000, 128, False, 0, 0, 100, 1900, 3, 700),    # chunks not on tile bounds
     (1, 1, 100, 500, 64, False, 0, 0, 0, None, 6, 128),        # chunks past the range
+    (2, 4, 1, 5000, 128, True, 4999, 0, 0, None, 7, 768),     # one row per slice
+    (1, 2, 24, 3000, 64, True, 2976, 500, 0, None, 4, 832),   # 24 rows, window
     (2, 8, 256, 3000, 128, True, 2744, 0, 0, None, 3, 1024),   # 16 slices
 ]
 
@@ -251,6 +295,8 @@ GQA = [
     (1, 4, 2, 200, 600, 64, True, 400, 150),     # window
     (1, 4, 4, 300, 300, 128, True, 0, 0),        # H_kv = H
     (1, 16, 2, 40, 900, 128, True, 860, 64),     # 8 heads of 40 rows per slice
+    (1, 8, 2, 8, 1000, 64, True, 992, 0),        # 4 heads of 8 rows: 32 rows per slice
+    (1, 12, 4, 10, 700, 128, True, 690, 0),      # 3 heads of 10 rows per slice
 ]
 
 

@@ -99,7 +99,7 @@ def test_random_extended(seed):
     check(o, lse, o_ref, lse_ref, c["dtype"], f"ext {c}")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(12))
 def test_random_scaled(seed):
     rng = random.Random(3000 + seed)
     qk = rng.choice(["fp8_e4m3", "bf16", "f16"])
@@ -113,6 +113,10 @@ def test_random_scaled(seed):
     q, k, v, qs, ks = scaled_inputs(c["B"], c["H"], c["S_q"], c["S_k"], c["D_qk"], c["D_v"],
                                     c["q_block"], c["k_block"], qk, vdt, seed=seed,
                                     scale_jitter=True)
+    # block scales of either sign (and some zero), drawn per block
+    g = torch.Generator(device="cpu").manual_seed(3100 + seed)
+    ks = (ks * torch.randint(-1, 2, ks.shape, generator=g).float()).contiguous()
+    qs = (qs * torch.where(torch.rand(qs.shape, generator=g) < 0.25, -1.0, 1.0)).contiguous()
     o, lse = tsd.attn_fwd_scaled(q.to(DEV), k.to(DEV), v.to(DEV), qs.to(DEV), ks.to(DEV),
                                  c["q_block"], c["k_block"], c["causal"])
     torch.cuda.synchronize()
