@@ -18,7 +18,10 @@ Before the warm-up steps the step runs back to back for --settle-s seconds
 (default 1): an idle MI355X starts at a low engine clock and needs tens of
 launches of the headline size to reach the clock it holds under this load,
 so a handful of warm-up steps alone leaves the ramp inside the timed steps.
-The timed region is exactly --steps steps either way.
+The timed region is exactly --steps steps either way, with nothing else
+enqueued between its launches; a second pass of the same steps, with a HIP
+event before every launch, gives how a step divides between its launches
+(`attn_ms_in_step`, and `merge_ms` for split-KV).
 
 --workload also selects the extended entry points' workloads (key offset,
 sliding window, split-KV with its merge, grouped K/V heads); their FLOPs
@@ -492,18 +495,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # events before every launch and after the last: per-launch durations
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
-          for _ in range(args.steps)]
+    # The timed steps: nothing but the launches between the two
+    # synchronisations (an event recorded between launches is a marker
+    # packet of its own, which would count in the step time).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # The same steps again with events before every launch and after the
+    # last: how the step divides between its launches.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+          for _ in range(args.steps)]
     for i in range(args.steps):
         for j, ph in enumerate(phases):
             ev[i][j].record(stream)
             ph()
         ev[i][-1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     launch_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps
                  for j in range(len(phases))]
     # The attention launch alone, `steps` times back to back between two
