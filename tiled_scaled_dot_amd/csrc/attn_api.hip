@@ -173,7 +173,7 @@ int check_ext_inputs(const void *Q, const void *K, const void *V, const ExtShape
     if (!Q || !K || !V) return TSD_ERR_NULL;
     if (es.B < 1 || es.H < 1 || es.H_kv < 1 || es.S_q < 1 || es.H % es.H_kv != 0)
         return TSD_ERR_SHAPE;
-    if (es.rows() > INT32_MAX) return TSD_ERR_UNSUPPORTED;
+    if (es.S_q > INT32_MAX / es.group()) return TSD_ERR_UNSUPPORTED;   // rows() fits int32
     const int st = check_shape(es.B, es.H_kv, es.rows(), es.S_k, es.D_qk, es.D_v, dtype);
     if (st != TSD_OK) return st;
     if (!std::isfinite(scale)) return TSD_ERR_SCALE;
@@ -455,7 +455,7 @@ extern "C" int attn_splitkv_plan(int64_t B, int64_t H, int64_t H_kv, int64_t S_q
     if (!splits_out || !split_len_out || !workspace_bytes) return TSD_ERR_NULL;
     const ExtShape es{B, H, H_kv, S_q, S_k, D_qk, D_v};
     if (B < 1 || H < 1 || H_kv < 1 || S_q < 1 || H % H_kv != 0) return TSD_ERR_SHAPE;
-    if (es.rows() > INT32_MAX) return TSD_ERR_UNSUPPORTED;
+    if (es.S_q > INT32_MAX / es.group()) return TSD_ERR_UNSUPPORTED;   // rows() fits int32
     int st = check_shape(B, H_kv, es.rows(), S_k, D_qk, D_v, dtype);
     if (st != TSD_OK) return st;
     if (dtype == TSD_F32 || !vector_dims_ok(dtype, D_qk, D_v)) return TSD_ERR_UNSUPPORTED;
