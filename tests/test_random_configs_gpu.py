@@ -4,8 +4,13 @@ so that the oracle checks every output (a few million score elements at
 most) while covering ragged sizes, head-dim tails, D_qk != D_v, both 16-bit
 dtypes, causal offsets, windows, key ranges, grouped heads and chunk
 counts; a last group draws grids of up to 6000 x 6000 per slice and checks
-a row sample."""
+a row sample.
+
+TSD_RANDOM_SEEDS=N in the environment widens every group to at least N
+seeds (a longer sweep of the same generators; the default keeps the suite
+short)."""
 import math
+import os
 import random
 
 import numpy as np
@@ -20,6 +25,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TOL_O = {"f32": 1e-4, "f16": 2e-2, "bf16": 2e-2}
 TOL_LSE = {"f32": 1e-4, "f16": 1e-3, "bf16": 1e-3}
+N_SEEDS = int(os.environ.get("TSD_RANDOM_SEEDS", "0"))
+
+
+def seeds(default):
+    return range(max(default, N_SEEDS))
 
 
 def to_np(t):
@@ -61,7 +71,7 @@ def draw_ext(rng):
                 n_splits=rng.choice([1, 1, 2, 3, 7]))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", seeds(12))
 def test_random_plain(seed):
     rng = random.Random(1000 + seed)
     c = draw_plain(rng)
@@ -75,7 +85,7 @@ def test_random_plain(seed):
     check(o, lse, o_ref, lse_ref, c["dtype"], f"plain {c}")
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", seeds(16))
 def test_random_extended(seed):
     rng = random.Random(2000 + seed)
     c = draw_ext(rng)
@@ -99,7 +109,7 @@ def test_random_extended(seed):
     check(o, lse, o_ref, lse_ref, c["dtype"], f"ext {c}")
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", seeds(12))
 def test_random_scaled(seed):
     rng = random.Random(3000 + seed)
     qk = rng.choice(["fp8_e4m3", "bf16", "f16"])
@@ -136,7 +146,7 @@ def draw_large(rng):
                 scale=rng.choice([1 / math.sqrt(D_qk), rng.uniform(-0.4, 0.4)]))
 
 
-@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("seed", seeds(10))
 def test_random_large_sampled_rows(seed):
     """Grids of up to a few thousand rows and keys (many key tiles, several
     workgroups per CU), every output computed on the GPU and a random sample
