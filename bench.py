@@ -23,6 +23,10 @@ enqueued between its launches; a second pass of the same steps, with a HIP
 event before every launch, gives how a step divides between its launches
 (`attn_ms_in_step`, and `merge_ms` for split-KV).
 
+--power-s S (off by default) adds `power`: the GPU's socket power, its
+power limit and the graphics clock, read in-process through amdsmi while
+the step runs back to back for S seconds after the measurements.
+
 --workload also selects the extended entry points' workloads (key offset,
 sliding window, split-KV with its merge, grouped K/V heads); their FLOPs
 count 2*(D_qk+D_v) per visible (query, key) pair, and a split-KV step is
@@ -71,6 +75,11 @@ def parse():
                          "(torch.matmul, the platform's GEMM library) after the clock settle "
                          "and print their rate: the MFMA rate a plain dense contraction "
                          "sustains on this GPU, for comparison")
+    ap.add_argument("--power-s", type=float, default=0.0,
+                    help="after the timed steps (or the --gemm-probe launches), run the step back "
+                         "to back for this many seconds while a thread reads the GPU's socket "
+                         "power, power limit and graphics clock in-process (amdsmi) every 10 ms; "
+                         "report their means as `power` (off by default)")
     ap.add_argument("--record-traffic", nargs=4, metavar=("ATTN_FETCH", "ATTN_WRITE",
                                                           "COPY_FETCH", "COPY_WRITE"),
                     help="write the HBM traffic per launch into the stored traffic record "
@@ -141,7 +150,71 @@ def copy_probe(mib: int, launches: int) -> int:
     return 0
 
 
-def gemm_probe(n: int, launches: int, settle_s: float) -> int:
+class PowerReader:
+    """Socket power and graphics clock of the GPU torch uses as cuda:0, read
+    in-process through amdsmi (no child process) by a thread every 10 ms
+    while `run(step, seconds)` launches the step back to back.  The first
+    quarter of the samples (the ramp) is left out of the means."""
+
+    def __init__(self):
+        import amdsmi
+        import torch
+
+        self.smi = amdsmi
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+        bus = getattr(torch.cuda.get_device_properties(0), "pci_bus_id", None)
+        handles = amdsmi.amdsmi_get_processor_handles()
+        self.h = handles[0]
+        for h in handles:
+            if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == bus:
+                self.h = h
+        self.bdf = amdsmi.amdsmi_get_gpu_device_bdf(self.h)
+
+    def run(self, step, seconds: float) -> dict:
+        import threading
+
+        import torch
+
+        smi, samples, stop = self.smi, [], threading.Event()
+
+        def sample():
+            while not stop.is_set():
+                p = smi.amdsmi_get_power_info(self.h)
+                c = smi.amdsmi_get_clock_info(self.h, smi.AmdSmiClkType.GFX)
+                samples.append((float(p["current_socket_power"]), float(p["power_limit"]) / 1e6,
+                                float(c["clk"])))
+                time.sleep(0.01)
+
+        th = threading.Thread(target=sample, daemon=True)
+        t0 = time.perf_counter()
+        launches = 0
+        th.start()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                step()
+            launches += 4
+            torch.cuda.synchronize()
+        stop.set()
+        th.join()
+        kept = samples[len(samples) // 4:]
+        if not kept:
+            return {"error": "no samples"}
+        mean = lambda i: sum(x[i] for x in kept) / len(kept)
+        return {"socket_w_mean": round(mean(0), 1), "socket_w_max": max(x[0] for x in kept),
+                "power_limit_w": round(kept[-1][1], 1), "gfx_mhz_mean": round(mean(2), 1),
+                "samples": len(kept), "seconds": round(time.perf_counter() - t0, 2),
+                "launches": launches, "device_bdf": self.bdf, "source": "amdsmi, in-process"}
+
+
+def power_reading(step, seconds: float) -> dict:
+    """PowerReader().run(step, seconds), or the reason it could not run."""
+    try:
+        return PowerReader().run(step, seconds)
+    except Exception as e:   # amdsmi missing or not permitted here
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
+def gemm_probe(n: int, launches: int, settle_s: float, power_s: float = 0.0) -> int:
     """Time `launches` bf16 n x n x n products C = A B (torch.matmul, which
     calls the platform GEMM library) back to back between two events, after
     running them for `settle_s` seconds; print the rate and its fraction of
@@ -165,10 +238,12 @@ def gemm_probe(n: int, launches: int, settle_s: float) -> int:
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / launches
     tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-    print(json.dumps({"gemm_probe": f"bf16 {n}x{n}x{n}", "launches": launches, "ms": round(ms, 4),
-                      "tflops": round(tflops, 1),
-                      "frac_of_dense_bf16_peak": round(tflops / PEAK_TFLOPS["bf16"], 4)}),
-          flush=True)
+    out = {"gemm_probe": f"bf16 {n}x{n}x{n}", "launches": launches, "ms": round(ms, 4),
+           "tflops": round(tflops, 1),
+           "frac_of_dense_bf16_peak": round(tflops / PEAK_TFLOPS["bf16"], 4)}
+    if power_s > 0:
+        out["power"] = power_reading(lambda: torch.matmul(a, b, out=c), power_s)
+    print(json.dumps(out), flush=True)
     return 0
 
 
@@ -406,7 +481,7 @@ def main():
     if args.copy_probe_mib:
         return copy_probe(args.copy_probe_mib, args.steps)
     if args.gemm_probe:
-        return gemm_probe(args.gemm_probe, args.steps, args.settle_s)
+        return gemm_probe(args.gemm_probe, args.steps, args.settle_s, args.power_s)
 
     import torch
 
@@ -527,6 +602,7 @@ def main():
     torch.cuda.synchronize()
     kernel_ms = a0.elapsed_time(a1) / args.steps
     extra["attn_ms_in_step"] = round(launch_ms[0], 4)
+    power = power_reading(step, args.power_s) if args.power_s > 0 else None
 
     ms_per_step = wall * 1e3 / args.steps
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -601,6 +677,8 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if power is not None:
+        result["power"] = power
     if not args.no_cpu_baseline:
         del qd, kd, vd, o, lse
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_row_stride,
