@@ -402,7 +402,8 @@ def attn_fwd_scaled(q, k, v, q_scale, k_scale, q_block, k_block, causal=False, o
     """Base-2 attention with per-block scales: score = q_scale[b,h,i//q_block]
     * k_scale[b,h,j//k_block] * (q_i . k_j), weights 2^score.  q, k:
     float8_e4m3fn, or v's dtype (float16 / bfloat16); q_scale, k_scale:
-    float32 [B,H,ceil(S/block)], key scales >= 0; k_block a multiple of 64.
+    float32 [B,H,ceil(S/block)], finite, of either sign; k_block a multiple
+    of 64.
     Returns O (v's dtype) and LSE (float32, natural log)."""
     import torch
 
