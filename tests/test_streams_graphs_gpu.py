@@ -108,3 +108,46 @@ def test_graph_replay_matches_eager():
         for n, (o, l) in outs.items():
             assert torch.equal(got[n][0], o), f"replay {replay}: {n} O differs from eager"
             assert torch.equal(got[n][1], l), f"replay {replay}: {n} LSE differs from eager"
+
+
+def test_graph_replay_noalloc_splitkv():
+    """attn_fwd_splitkv_noalloc, the entry point for callers that cannot
+    allocate (graph capture among them), captured into a graph after one
+    eager call (which looks up the device's scratch array) and replayed
+    three times with new inputs; each replay equals the eager call and the
+    workspace form of split-KV on the same inputs."""
+    B, H, H_kv, S_q, S_k, D = 2, 16, 4, 4, 9000, 128
+    q, k, v = gpu(*random_inputs((B, H, S_q, D), (B, H_kv, S_k, D), (B, H_kv, S_k, D),
+                                 "bf16", seed=31))
+    kw = dict(causal=True, causal_offset=S_k - S_q, n_splits=6)
+    out = torch.empty((B, H, S_q, D), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((B, H, S_q), dtype=torch.float32, device=DEV)
+
+    def call():
+        tsd.attn_fwd_splitkv_noalloc(q, k, v, out=out, lse=lse, **kw)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+
+    g = torch.Generator(device="cpu").manual_seed(32)
+    for replay in range(3):
+        q.copy_(torch.randn(q.shape, generator=g).to(q.dtype))
+        v.copy_(torch.randn(v.shape, generator=g).to(v.dtype))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_l = out.clone(), lse.clone()
+        call()   # eager, same inputs
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, out) and torch.equal(got_l, lse), f"replay {replay}"
+        o_ws, l_ws = tsd.attn_fwd_splitkv(q, k, v, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(got_o, o_ws) and torch.equal(got_l, l_ws), f"replay {replay}"
