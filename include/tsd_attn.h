@@ -183,6 +183,12 @@ TSD_API int attn_fwd_plan_block(const tsd_plan *plan, int64_t S_q, int64_t S_k,
  * Invalid: kv_begin < 0, kv_end > S_k, kv_begin > kv_end, window < 0
  * (TSD_ERR_SHAPE); |causal_offset| or window above 2^30
  * (TSD_ERR_UNSUPPORTED).
+ * K and V rows that no query row of the call sees (outside [kv_begin,
+ * kv_end), after the last row's diagonal, before the first row's window)
+ * may hold anything, NaN and infinity included: they never reach a result
+ * (an unwritten cache tail after kv_end is fine).  Rows that some query row
+ * sees are inputs like any other (a NaN there is not masked for the rows
+ * that do not see it).
  */
 typedef struct tsd_mask {
     int64_t causal_offset;  /* causal: key j visible to row i iff j <= i + causal_offset */

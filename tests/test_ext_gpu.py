@@ -378,3 +378,52 @@ def test_window_and_complement_partition_causal(window):
     o_ref, l_ref = ref_ext(q, k, v, 0.09, True)
     check(to_np(om), to_np(lm), o_ref, l_ref, "bf16", f"window {window} + complement merged")
     check(to_np(o_all), to_np(l_all), o_ref, l_ref, "bf16", "plain causal")
+
+
+# Keys that no query row of the call sees may hold any bits: they are never
+# read into a result.  The cases fill them with NaN (K) and NaN or infinity
+# (V): an unwritten cache tail after kv_end, a prefix before kv_begin, the
+# keys after the last row's diagonal and before the first row's window.
+UNSEEN = [
+    # B, H, H_kv, S_q, S_k, D, causal, causal_offset, window, kv_begin, kv_end, entry
+    (2, 8, 2, 1, 5000, 128, True, 3000, 0, 0, 3001, "ext"),         # decoding, cache tail
+    (2, 8, 2, 1, 5000, 128, True, 3000, 0, 0, 3001, "splitkv"),
+    (2, 8, 2, 1, 5000, 128, True, 3000, 0, 0, 3001, "noalloc"),
+    (1, 4, 4, 40, 2100, 64, False, 0, 0, 100, 2000, "ext"),         # prefix and tail
+    (1, 4, 4, 40, 2100, 64, False, 0, 0, 100, 2000, "splitkv"),
+    (1, 2, 2, 300, 1000, 128, True, 500, 200, 0, None, "ext"),      # diagonal and window
+    (1, 6, 3, 7, 777, 128, True, 700, 0, 37, 701, "splitkv"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("case", UNSEEN, ids=[f"u{i}" for i in range(len(UNSEEN))])
+def test_unseen_keys_never_reach_results(case, dtype):
+    B, H, H_kv, S_q, S_k, D, causal, coff, window, kb, ke, entry = case
+    print(f"[case] unseen keys {case} {dtype}", flush=True)
+    q, k, v = random_inputs((B, H, S_q, D), (B, H_kv, S_k, D), (B, H_kv, S_k, D), dtype,
+                            seed=7000 + S_k + S_q)
+    ke_ = S_k if ke is None else ke
+    # keys no row sees: outside [kb, ke), after the last row's diagonal,
+    # before the first row's window
+    seen_lo = max(kb, coff - window + 1) if window > 0 else kb
+    seen_hi = min(ke_, S_q - 1 + coff + 1) if causal else ke_
+    unseen = torch.ones(S_k, dtype=torch.bool)
+    unseen[seen_lo:seen_hi] = False
+    assert unseen.any()
+    k[:, :, unseen] = float("nan")
+    v[:, :, unseen] = float("nan")
+    v[:, :, unseen.nonzero()[::2, 0]] = float("inf")
+    scale = 1 / math.sqrt(D)
+    kw = dict(scale=scale, causal=causal, causal_offset=coff, window=window, kv_begin=kb,
+              kv_end=ke)
+    qg, kg, vg = gpu(q, k, v)
+    if entry == "ext":
+        o, lse = tsd.attn_fwd_ext(qg, kg, vg, **kw)
+    elif entry == "splitkv":
+        o, lse = tsd.attn_fwd_splitkv(qg, kg, vg, n_splits=3, **kw)
+    else:
+        o, lse = tsd.attn_fwd_splitkv_noalloc(qg, kg, vg, **kw)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = ref_ext(q, k, v, scale, causal, coff, window, kb, ke)
+    check(to_np(o), to_np(lse), o_ref, lse_ref, dtype, f"unseen keys {case} {dtype}")

@@ -949,11 +949,15 @@ attn_fwd_fast16(KernelArgs p)
         khi = min(p.kv_end, klo + p.split_len);
     }
 
-    // key tiles of this workgroup: t_first .. t_first + ntiles - 1
+    // key tiles of this workgroup: t_first .. t_first + ntiles - 1, holding
+    // the keys [wg_lo, wg_hi) some row of it sees
     int t_first = 0, ntiles;
+    int32_t wg_lo = 0, wg_hi = p.S_k;
     if constexpr (EXT) {
         const PosRange pr = row_positions(q0, min(q0 + T::BM, p.S_q), p.q_per_head);
         const KeyRange kr = wg_key_range(pr.lo, pr.hi + 1, klo, khi, CAUSAL, p.coff, p.window);
+        wg_lo = kr.key_lo;
+        wg_hi = kr.key_hi;
         t_first = kr.key_lo / BN;
         ntiles = kr.key_hi > kr.key_lo ? (kr.key_hi + BN - 1) / BN - t_first : 0;
     } else {
@@ -965,8 +969,14 @@ attn_fwd_fast16(KernelArgs p)
     const uint32_t v_bytes = (uint32_t)p.S_k * p.D_v * 2;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(static_cast<const uint8_t *>(p.Q) + (size_t)slice * q_bytes, q_bytes);
-    const u32x4 rk = rsrc_words(static_cast<const uint8_t *>(p.K) + (size_t)slice * k_bytes, k_bytes);
-    const u32x4 rv = rsrc_words(static_cast<const uint8_t *>(p.V) + (size_t)slice * v_bytes, v_bytes);
+    // K and V are read through ranges that end at the workgroup's last
+    // visible key (the slice's end in the plain kernel): the keys after it
+    // that share its tile read as zero, so that whatever the caller keeps
+    // there (an unwritten cache tail, NaN) never reaches a result.
+    const uint32_t k_range = EXT ? (uint32_t)wg_hi * p.D_qk * QKB : k_bytes;
+    const uint32_t v_range = EXT ? (uint32_t)wg_hi * p.D_v * 2 : v_bytes;
+    const u32x4 rk = rsrc_words(static_cast<const uint8_t *>(p.K) + (size_t)slice * k_bytes, k_range);
+    const u32x4 rv = rsrc_words(static_cast<const uint8_t *>(p.V) + (size_t)slice * v_bytes, v_range);
 
     // ---- per-lane source offsets of this wave's K/V load instructions
     // (waves past DMA_WAVES issue no loads; their offsets are those of wave 0)
@@ -1011,6 +1021,38 @@ attn_fwd_fast16(KernelArgs p)
             for (int j = 0; j < T::V_PER_W; ++j) dma16(lds_v0 + sl + j * 1024, voff[j], r);
         }
     };
+    // Tile 0 into slot 0.  In the extended kernel the rows of the first
+    // tile before the workgroup's first visible key read as zero as well
+    // (the counterpart of the range end above).
+    const int skip0 = EXT ? wg_lo - t_first * BN : 0;   // rows of tile 0 before wg_lo
+    auto issue_k0 = [&]() __attribute__((always_inline)) {
+        if (EXT && skip0 > 0) {
+            const u32x4 r = tile_rsrc(rk, (uint32_t)t_first * BN * p.D_qk * QKB);
+            if (dma_wave) {
+#pragma unroll
+                for (int j = 0; j < T::K_PER_W; ++j) {
+                    const int row = ((dw * T::K_PER_W + j) * 64 + lane) / T::KCH;
+                    dma16(lds_k0 + j * 1024, row < skip0 ? kOutOfRange : koff[j], r);
+                }
+            }
+        } else {
+            issue_k(0, IC<0>{});
+        }
+    };
+    auto issue_v0 = [&]() __attribute__((always_inline)) {
+        if (EXT && skip0 > 0) {
+            const u32x4 r = tile_rsrc(rv, (uint32_t)t_first * BN * p.D_v * 2);
+            if (dma_wave) {
+#pragma unroll
+                for (int j = 0; j < T::V_PER_W; ++j) {
+                    const int row = ((dw * T::V_PER_W + j) * 64 + lane) / T::VCH;
+                    dma16(lds_v0 + j * 1024, row < skip0 ? kOutOfRange : voff[j], r);
+                }
+            }
+        } else {
+            issue_v(0, IC<0>{});
+        }
+    };
 
     // Output of this slice (of chunk `split` when the output is partial).
     constexpr uint32_t o_elt = OUT_F32 ? 4u : 2u;
@@ -1050,19 +1092,20 @@ attn_fwd_fast16(KernelArgs p)
     static_assert(!BAR2 || (T::KS == 4 && T::VS == 4), "BAR2 needs four-tile rings");
     if constexpr (BAR2) {
         // K(0..2) and V(0..1): the tiles of iterations 0 and 1
-        issue_k(0, IC<0>{});
+        issue_k0();
         if (1 < ntiles) issue_k(1, IC<1>{});
         if (2 < ntiles) issue_k(2, IC<2>{});
-        issue_v(0, IC<0>{});
+        issue_v0();
         if (1 < ntiles) issue_v(1, IC<1>{});
     } else {
     // Prologue: K(0 .. KS-1) and V(0 .. VS-2) in the order the main loop
     // would have issued them (K(j) before V(j-1)), K(0) first.
-    issue_k(0, IC<0>{});
+    issue_k0();
     static_for<1, T::KS>([&](auto jc) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value;
         if (j < ntiles) issue_k(j, IC<j>{});
-        if constexpr (j - 1 < T::VS - 1)
+        if constexpr (j == 1) issue_v0();
+        else if constexpr (j - 1 < T::VS - 1)
             if (j - 1 < ntiles) issue_v(j - 1, IC<j - 1>{});
     });
     }
