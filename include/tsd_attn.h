@@ -97,7 +97,9 @@ typedef struct tsd_plan {
  *   scale  any finite float (0 and negative allowed); multiplies the dot
  *       product.
  *   causal 0 or nonzero (top-left: key j visible to query i iff j <= i).
- *   stream a hipStream_t (NULL = the null stream).
+ *   stream a hipStream_t of the current device (NULL = its null stream);
+ *       the kernels run on the current device, so every buffer must live
+ *       there (or be accessible from it).
  *
  * Ownership: the caller allocates and frees every buffer; the library
  * allocates no device memory, keeps no pointer after returning, and never

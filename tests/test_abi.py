@@ -416,3 +416,15 @@ def test_planner_and_checks_from_many_threads(lib):
 
     with ThreadPoolExecutor(8) as ex:
         assert all(ex.map(worker, range(8)))
+
+
+def test_binding_rejects_tensors_on_two_devices():
+    """The binding refuses a call whose tensors live on different devices
+    (a kernel would otherwise read another device's memory)."""
+    import torch
+
+    a = torch.empty(1)
+    b = torch.empty(1, device="meta")
+    tsd._one_device(a, k=a, v=None)
+    with pytest.raises(ValueError, match="meta"):
+        tsd._one_device(a, k=b)

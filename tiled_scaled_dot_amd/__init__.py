@@ -236,6 +236,7 @@ def _qkv(q, k, v, grouped=False):
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    _one_device(q, k=k, v=v)
     B, H, S_q, D_qk = q.shape
     S_k, D_v = k.shape[2], v.shape[3]
     H_kv = k.shape[1] if grouped else H
@@ -268,6 +269,21 @@ def _stream(stream, device):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
 
+def _one_device(first, **others):
+    """Every tensor of a call must live on the first one's device."""
+    for name, t in others.items():
+        if t is not None and t.device != first.device:
+            raise ValueError(f"{name} is on {t.device}, the call's tensors on {first.device}")
+
+
+def _on(t):
+    """Make t's device the current one for the call: the library launches on
+    the current device, into a stream of that device."""
+    import torch
+
+    return torch.cuda.device(t.device)
+
+
 def attn_fwd_ext(q, k, v, scale=None, causal=False, causal_offset=0, window=0, kv_begin=0,
                  kv_end=None, out=None, lse=None, stream=None):
     """attn_fwd restricted per row to the keys of the mask (see TsdMask);
@@ -282,9 +298,10 @@ def attn_fwd_ext(q, k, v, scale=None, causal=False, causal_offset=0, window=0, k
     out = _buffer(out, (B, H, S_q, D_v), q.dtype, q, "out")
     lse = _buffer(lse, (B, H, S_q), torch.float32, q, "lse")
     mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
-    _check(attn_fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
-                            code, mask, _stream(stream, q.device)))
+    with _on(q):
+        _check(attn_fwd_ext_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
+                                code, mask, _stream(stream, q.device)))
     return out, lse
 
 
@@ -302,10 +319,11 @@ def attn_fwd_partial(q, k, v, n_splits, split_len, scale=None, causal=False, cau
     o_parts = _buffer(o_parts, (n_splits, B, H, S_q, D_v), torch.float32, q, "o_parts")
     lse_parts = _buffer(lse_parts, (n_splits, B, H, S_q), torch.float32, q, "lse_parts")
     mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
-    _check(attn_fwd_partial_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts.data_ptr(),
-                                lse_parts.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale,
-                                causal, code, mask, n_splits, split_len,
-                                _stream(stream, q.device)))
+    with _on(q):
+        _check(attn_fwd_partial_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_parts.data_ptr(),
+                                    lse_parts.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale,
+                                    causal, code, mask, n_splits, split_len,
+                                    _stream(stream, q.device)))
     return o_parts, lse_parts
 
 
@@ -324,11 +342,13 @@ def attn_merge(o_parts, lse_parts, dtype=None, out=None, lse=None, stream=None):
             raise ValueError(f"{name} must be a contiguous float32 GPU tensor")
     if tuple(lse_parts.shape) != (n, B, H, S_q):
         raise ValueError("lse_parts shape does not match o_parts")
+    _one_device(o_parts, lse_parts=lse_parts)
     out = _buffer(out, (B, H, S_q, D_v), dtype, o_parts, "out")
     lse = _buffer(lse, (B, H, S_q), torch.float32, o_parts, "lse")
-    _check(attn_merge_raw(o_parts.data_ptr(), lse_parts.data_ptr(), n, B, H, S_q, D_v,
-                          out.data_ptr(), lse.data_ptr(), codes[dtype],
-                          _stream(stream, o_parts.device)))
+    with _on(o_parts):
+        _check(attn_merge_raw(o_parts.data_ptr(), lse_parts.data_ptr(), n, B, H, S_q, D_v,
+                              out.data_ptr(), lse.data_ptr(), codes[dtype],
+                              _stream(stream, o_parts.device)))
     return out, lse
 
 
@@ -349,12 +369,14 @@ def attn_fwd_splitkv(q, k, v, scale=None, causal=False, causal_offset=0, window=
                                  H_kv=H_kv)
     if workspace is None and ws > 0:
         workspace = torch.empty(ws, dtype=torch.uint8, device=q.device)
+    _one_device(q, workspace=workspace)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(attn_fwd_splitkv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                lse.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
-                                code, mask, n_splits, ws_ptr, ws_bytes,
-                                _stream(stream, q.device)))
+    with _on(q):
+        _check(attn_fwd_splitkv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, H, H_kv, S_q, S_k, D_qk, D_v, scale, causal,
+                                    code, mask, n_splits, ws_ptr, ws_bytes,
+                                    _stream(stream, q.device)))
     return out, lse
 
 
@@ -382,10 +404,11 @@ def attn_fwd_splitkv_noalloc(q, k, v, scale=None, causal=False, causal_offset=0,
     out = _buffer(out, (B, H, S_q, D_v), q.dtype, q, "out")
     lse = _buffer(lse, (B, H, S_q), torch.float32, q, "lse")
     mask = make_mask(S_k, causal_offset, window, kv_begin, kv_end)
-    _check(attn_fwd_splitkv_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                        out.data_ptr(), lse.data_ptr(), B, H, H_kv, S_q, S_k,
-                                        D_qk, D_v, scale, causal, code, mask, n_splits,
-                                        _stream(stream, q.device)))
+    with _on(q):
+        _check(attn_fwd_splitkv_noalloc_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            out.data_ptr(), lse.data_ptr(), B, H, H_kv, S_q, S_k,
+                                            D_qk, D_v, scale, causal, code, mask, n_splits,
+                                            _stream(stream, q.device)))
     return out, lse
 
 
@@ -416,6 +439,7 @@ def attn_fwd_scaled(q, k, v, q_scale, k_scale, q_block, k_block, causal=False, o
     for name, t in (("q", q), ("k", k), ("v", v), ("q_scale", q_scale), ("k_scale", k_scale)):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous GPU tensor")
+    _one_device(v, q=q, k=k, q_scale=q_scale, k_scale=k_scale)
     B, H, S_q, D_qk = q.shape
     S_k, D_v = k.shape[2], v.shape[3]
     if tuple(k.shape) != (B, H, S_k, D_qk) or tuple(v.shape) != (B, H, S_k, D_v):
@@ -426,10 +450,11 @@ def attn_fwd_scaled(q, k, v, q_scale, k_scale, q_block, k_block, causal=False, o
         raise ValueError(f"q_scale must be float32 [{B},{H},{nq}] and k_scale [{B},{H},{nk}]")
     out = _buffer(out, (B, H, S_q, D_v), v.dtype, v, "out")
     lse = _buffer(lse, (B, H, S_q), torch.float32, v, "lse")
-    _check(attn_fwd_scaled_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                               lse.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), B, H, S_q,
-                               S_k, D_qk, D_v, q_block, k_block, causal, qk_code,
-                               vcodes[v.dtype], _stream(stream, v.device)))
+    with _on(v):
+        _check(attn_fwd_scaled_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), q_scale.data_ptr(), k_scale.data_ptr(), B, H,
+                                   S_q, S_k, D_qk, D_v, q_block, k_block, causal, qk_code,
+                                   vcodes[v.dtype], _stream(stream, v.device)))
     return out, lse
 
 
@@ -454,6 +479,7 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None)
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    _one_device(q, k=k, v=v)
     B, H, S_q, D_qk = q.shape
     S_k, D_v = k.shape[2], v.shape[3]
     if tuple(k.shape) != (B, H, S_k, D_qk) or tuple(v.shape) != (B, H, S_k, D_v):
@@ -475,8 +501,9 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None, stream=None)
         stream = torch.cuda.current_stream(q.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    status = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                          lse.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal,
-                          codes[q.dtype], stream)
+    with _on(q):
+        status = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, H, S_q, S_k, D_qk, D_v, scale, causal,
+                              codes[q.dtype], stream)
     _check(status)
     return out, lse
