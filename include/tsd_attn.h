@@ -95,7 +95,8 @@ typedef struct tsd_plan {
  *   LSE [B,H,S_q] contiguous f32 device buffer, natural log of the softmax
  *       denominator of the scaled scores; may be NULL (then not written).
  *   scale  any finite float (0 and negative allowed); multiplies the dot
- *       product.
+ *       product.  Scores are formed in f32: a |scale * q.k| beyond the f32
+ *       range (about 3.4e38) overflows.
  *   causal 0 or nonzero (top-left: key j visible to query i iff j <= i).
  *   stream a hipStream_t of the current device (NULL = its null stream);
  *       the kernels run on the current device, so every buffer must live
