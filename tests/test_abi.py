@@ -428,3 +428,56 @@ def test_binding_rejects_tensors_on_two_devices():
     tsd._one_device(a, k=a, v=None)
     with pytest.raises(ValueError, match="meta"):
         tsd._one_device(a, k=b)
+
+
+# ------------------------------------------------- planner over any sizes
+from hypothesis import given, settings, strategies as st  # noqa: E402
+
+_dims = st.one_of(st.integers(-2, 3), st.integers(1, 1 << 14), st.integers(1, 1 << 40),
+                  st.sampled_from([(1 << 31) - 1, 1 << 31, (1 << 32) + 1, 1 << 62]))
+
+
+@settings(max_examples=600, deadline=None)
+@given(B=_dims, H=_dims, S_q=_dims, S_k=_dims, D_qk=st.integers(-1, 260),
+       D_v=st.integers(-1, 260), dtype=st.integers(-1, 4), causal=st.booleans())
+def test_planner_total_over_any_sizes(lib, B, H, S_q, S_k, D_qk, D_v, dtype, causal):
+    """Whatever the sizes (negative, zero, up to 2^62), the planner returns a
+    status instead of overflowing: SHAPE for a dimension below 1, otherwise
+    OK or UNSUPPORTED, and an accepted plan fits the kernels' 32-bit grid
+    and in-slice offsets."""
+    try:
+        plan = tsd.attn_fwd_plan(B, H, S_q, S_k, D_qk, D_v, causal, dtype)
+    except tsd.TsdError as e:
+        if min(B, H, S_q, S_k, D_qk, D_v) < 1:
+            assert e.status == 2
+        else:
+            assert e.status == 3
+        return
+    assert min(B, H, S_q, S_k, D_qk, D_v) >= 1 and dtype in (0, 1, 2)
+    elt = 4 if dtype == 0 else 2
+    assert max(S_q, S_k) * max(D_qk, D_v) * elt < (1 << 31)
+    assert plan.slices == B * H and plan.q_blocks == -(-S_q // plan.block_m)
+    assert plan.grid == plan.q_blocks * plan.slices < (1 << 31)
+
+
+@settings(max_examples=400, deadline=None)
+@given(B=_dims, H_kv=st.integers(1, 64), group=st.integers(1, 64), S_q=_dims, S_k=_dims,
+       D=st.sampled_from([8, 64, 128, 136]), causal=st.booleans(),
+       coff=st.integers(-(1 << 31), 1 << 31), window=st.integers(-1, 1 << 31),
+       n_splits=st.integers(-1, 300))
+def test_splitkv_planner_total_over_any_sizes(lib, B, H_kv, group, S_q, S_k, D, causal, coff,
+                                              window, n_splits):
+    """The split-KV planner under the same kind of sizes and any mask values:
+    a status, or a plan whose chunks cover the key range in at most 256
+    whole-tile chunks."""
+    H = H_kv * group
+    try:
+        mask = tsd.make_mask(max(S_k, 0), coff, window)
+        n, ln, ws = tsd.attn_splitkv_plan(B, H, S_q, S_k, D, D, causal, "bf16", mask,
+                                          n_splits, H_kv=H_kv)
+    except tsd.TsdError as e:
+        assert e.status in (2, 3)
+        return
+    assert 1 <= n <= 256 and ln % 64 == 0 and ln >= 64
+    assert (n - 1) * ln < max(S_k, 1) <= n * ln or n == 1
+    assert ws >= 0
